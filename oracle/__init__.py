@@ -1,0 +1,171 @@
+"""CPU oracle for MoE dispatch / combine -- TEST INFRASTRUCTURE ONLY.
+
+A ctypes front end over ``oracle/oracle.c`` (plain C, built with
+``gcc -O2 -ffp-contract=off``).  Only the test suite, the smoke entry point
+and the benchmark's CPU-baseline leg may import this package; the HIP
+library never does, and this package never imports the HIP library.
+
+Functions take and return numpy arrays on the host.  The definitions, and the
+passages of the pages each one follows, are documented in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CONTIGUOUS = 0
+MASKED = 1
+QUANT_NONE = 0
+QUANT_FP8_F32 = 1
+QUANT_FP8_UE8M0 = 2
+
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+           "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_dispatch_layout.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64,
+                                           P, P, P, P, P, P, P, P]
+    lib.oracle_dispatch_layout.restype = ctypes.c_int
+    lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_dispatch.restype = None
+    lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_combine.restype = None
+    for name in ("oracle_bf16_rne_array", "oracle_e4m3_encode_array",
+                 "oracle_ue8m0_exponent_array"):
+        getattr(lib, name).argtypes = [P, P, i64]
+        getattr(lib, name).restype = None
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def rows_capacity(T: int, K: int, E: int, layout: int, align: int = 1,
+                  capacity: int = 1) -> int:
+    """Rows a dispatched buffer needs: T*K + E*(align-1) contiguous, E*C masked."""
+    return T * K + E * (align - 1) if layout == CONTIGUOUS else E * capacity
+
+
+def dispatch_layout(topk_idx: np.ndarray, E: int, R: int, layout: int,
+                    align: int = 1, capacity: int = 1,
+                    rows_cap: Optional[int] = None) -> dict:
+    """Counts, offsets, stable slots and both maps for int32 ids [T, K]."""
+    lib = _load()
+    idx = _c(topk_idx, np.int32)
+    T, K = idx.shape
+    if rows_cap is None:
+        rows_cap = rows_capacity(T, K, E, layout, align, capacity)
+    h = dict(expert_count=np.zeros(E, np.int32), recv_count=np.zeros(E, np.int32),
+             expert_offset=np.zeros(E + 1, np.int32), rank_offset=np.zeros(R + 1, np.int32),
+             pair_to_row=np.zeros(T * K, np.int32), row_to_pair=np.zeros(rows_cap, np.int32),
+             status=np.zeros(2, np.int32))
+    rc = lib.oracle_dispatch_layout(T, K, E, R, layout, align, capacity, rows_cap, _ptr(idx),
+                                    _ptr(h["expert_count"]), _ptr(h["recv_count"]),
+                                    _ptr(h["expert_offset"]), _ptr(h["rank_offset"]),
+                                    _ptr(h["pair_to_row"]), _ptr(h["row_to_pair"]),
+                                    _ptr(h["status"]))
+    if rc != 0:
+        raise ValueError("rows needed exceed rows_capacity")
+    return h
+
+
+def dispatch(x: np.ndarray, pair_to_row: np.ndarray, K: int, quant: int, rows: int,
+             topk_w: Optional[np.ndarray] = None, out_x: Optional[np.ndarray] = None,
+             out_scale: Optional[np.ndarray] = None,
+             out_row_weight: Optional[np.ndarray] = None):
+    """Permute (and optionally quantize) bf16 rows x [T, H] into `rows` rows.
+
+    Output buffers may be passed pre-filled (e.g. with a sentinel) to check
+    that unwritten rows stay untouched; otherwise they are zero-filled.
+    Returns (out_x, out_scale, out_row_weight).
+    """
+    lib = _load()
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    NB = H // 128
+    if out_x is None:
+        out_x = np.zeros((rows, H), np.uint16 if quant == QUANT_NONE else np.uint8)
+    if out_scale is None and quant == QUANT_FP8_F32:
+        out_scale = np.zeros((rows, NB), np.float32)
+    if out_scale is None and quant == QUANT_FP8_UE8M0:
+        out_scale = np.zeros((rows, (NB + 3) // 4), np.uint32)
+    w = None if topk_w is None else _c(topk_w, np.float32)
+    for a in (out_x, out_scale, out_row_weight):
+        assert a is None or a.flags["C_CONTIGUOUS"]
+    lib.oracle_dispatch(T, K, H, quant, _ptr(x), _ptr(w), _ptr(_c(pair_to_row, np.int32)),
+                        _ptr(out_x), _ptr(out_scale), _ptr(out_row_weight))
+    return out_x, out_scale, out_row_weight
+
+
+def combine(y: np.ndarray, topk_w: np.ndarray, pair_to_row: np.ndarray) -> np.ndarray:
+    """Weighted top-k reduction: bf16 y [rows, H] -> bf16 out [T, H] (uint16 bits)."""
+    lib = _load()
+    y = _c(y, np.uint16)
+    w = _c(topk_w, np.float32)
+    T, K = w.shape
+    H = y.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    lib.oracle_combine(T, K, H, _ptr(y), _ptr(w), _ptr(_c(pair_to_row, np.int32)), _ptr(out))
+    return out
+
+
+def bf16_rne(a: np.ndarray) -> np.ndarray:
+    lib = _load()
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib.oracle_bf16_rne_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_encode(a: np.ndarray) -> np.ndarray:
+    lib = _load()
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib.oracle_e4m3_encode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return _load().oracle_e4m3_value(code)
+
+
+def ue8m0_exponent(a: np.ndarray) -> np.ndarray:
+    lib = _load()
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.int32)
+    lib.oracle_ue8m0_exponent_array(_ptr(a), _ptr(out), a.size)
+    return out

@@ -1,0 +1,449 @@
+/*
+ * CPU oracle for MoE token dispatch / combine.  TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, obviously-correct definition that the HIP
+ * library is checked against.  Only the test suite, the smoke entry point and
+ * the benchmark's CPU-baseline leg may load it.  It shares no code, header,
+ * table or helper with the HIP library: it has its own bf16 / E4M3 / UE8M0
+ * codecs, written from the format definitions (IEEE-754 binary16-truncated
+ * "bfloat16" with round-to-nearest-even, and the OCP 8-bit floating point
+ * specification for E4M3 and E8M0), and its own layout arithmetic.
+ *
+ * Build: gcc -O2 -ffp-contract=off (no fast-math, SSE float on x86-64, so
+ * every float operation below is one correctly rounded IEEE binary32 op).
+ *
+ * What is computed, and the passages it follows (pages cited by title and
+ * section):
+ *   - Layout inferred from top-k expert ids, with per-expert received-token
+ *     counts carried on the dispatch handle: page "moe: add DeepEP V2
+ *     ElasticBuffer support to MoE token dispatcher", Motivation and the
+ *     _dispatch_core commit message.
+ *   - Per-expert-contiguous ("expanded") layout for prefill and the
+ *     fixed-capacity masked [experts, capacity, hidden] slab for decode:
+ *     page "[Feature] Add DeepEPv2 (ElasticBuffer) MoE A2A backend",
+ *     Supported scope / layouts paragraph and the review reply on layout
+ *     following the inference phase; page vLLM tools/ep_kernels, commit
+ *     message (do_expand, per-expert-contiguous layout).
+ *   - FP8 block-quantized dispatch with fp32 (Hopper) or packed UE8M0
+ *     (Blackwell) activation scales: page "[Feature] Add DeepEPv2
+ *     (ElasticBuffer) MoE A2A backend", Implementation; page "deepep v2
+ *     support?", quantization requirement (128x128 weight blocks, dynamic
+ *     activation scaling => 1x128 activation groups).
+ *   - Combine as the router-weighted top-k reduction back to token order,
+ *     with no further reduction after it: page vLLM tools/ep_kernels, commit
+ *     message (weighted reduction in combine); page "[Feature] Add DeepEPv2
+ *     (ElasticBuffer) MoE A2A backend", review (extra post-expert reduction
+ *     double-counts).
+ *
+ * The pages leave row order, alignment, overflow handling, scale formulas and
+ * rounding open; the readings taken here are listed in the design doc and in the
+ * comments of each function.  Every function below is pinned by a CPU test
+ * (brute force, closed forms, library routines, exhaustive codec sweeps or
+ * hand-worked fixtures); none is "parity unpinned".
+ */
+#include <assert.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Codecs                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 bits -> float: the bf16 pattern is the upper half of a binary32. */
+float oracle_bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t float_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* Value of a bf16 magnitude pattern (sign cleared) as a double, with the
+ * pattern one past the largest finite magnitude standing for 2^128 (where
+ * IEEE rounding sends overflowing values, i.e. to infinity). */
+static double bf16_mag_value(uint32_t mag)
+{
+    if (mag >= 0x7F80u)
+        return ldexp(1.0, 128);
+    return (double)oracle_bf16_to_float((uint16_t)mag);
+}
+
+/* float -> bfloat16 bits, round to nearest, ties to even.  Written as the
+ * definition: of the two bf16 magnitudes that bracket |f| (the truncation and
+ * its successor), take the nearer; on a tie take the one whose last mantissa
+ * bit is 0.  Differences are exact in double.  Inputs are finite. */
+uint16_t oracle_bf16_rne(float f)
+{
+    uint32_t u = float_bits(f);
+    uint32_t sign = u & 0x80000000u;
+    assert((u & 0x7F800000u) != 0x7F800000u); /* finite inputs only */
+    uint32_t lo = (u & 0x7FFFFFFFu) >> 16;    /* truncated magnitude */
+    uint32_t hi = lo + 1;
+    double a = fabs((double)f);
+    double dlo = a - bf16_mag_value(lo);
+    double dhi = bf16_mag_value(hi) - a;
+    uint32_t pick;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = hi;
+    else
+        pick = (lo & 1u) ? hi : lo;
+    return (uint16_t)((sign >> 16) | pick);
+}
+
+/* Value of a non-negative E4M3 code 0x00..0x7E (OCP FP8 E4M3: bias 7, three
+ * mantissa bits, exponent field 0 = subnormal m/8 * 2^-6, no infinities,
+ * 0x7F = NaN, largest finite 0x7E = 448). */
+double oracle_e4m3_value(uint8_t code)
+{
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    assert(code <= 0x7E);
+    if (e == 0)
+        return ldexp((double)m / 8.0, -6);
+    return ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/* Values of the 127 non-negative finite codes, filled from the decode rule
+ * above on first use. */
+static double e4m3_values[0x7F];
+static int e4m3_values_ready = 0;
+
+static double e4m3_code_value(int code)
+{
+    if (!e4m3_values_ready) {
+        for (int c = 0; c <= 0x7E; c++)
+            e4m3_values[c] = oracle_e4m3_value((uint8_t)c);
+        e4m3_values_ready = 1;
+    }
+    return e4m3_values[code];
+}
+
+/* float -> E4M3 byte, for finite |v| <= 448.  The definition: the code whose
+ * value is nearest to |v|, ties to the code with even (zero) last mantissa
+ * bit, sign bit = sign of v (so -0 and small negatives give 0x80).  The 127
+ * non-negative finite codes are increasing in value, so the bracketing pair is
+ * found by bisection over the code values. */
+uint8_t oracle_e4m3_encode(float v)
+{
+    uint8_t sign = (float_bits(v) & 0x80000000u) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    assert(a <= 448.0);
+    /* largest code c with value(c) <= a */
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (e4m3_code_value(mid) <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int c = lo;
+    if (c < 0x7E) {
+        double dlo = a - e4m3_code_value(c);
+        double dhi = e4m3_code_value(c + 1) - a;
+        if (dhi < dlo || (dhi == dlo && (c & 1)))
+            c = c + 1;
+    }
+    return (uint8_t)(sign | (uint8_t)c);
+}
+
+/* UE8M0 scale exponent: the smallest integer k with a <= 448 * 2^k, i.e. the
+ * power-of-two scale rounded UP so that no element of the block can exceed
+ * the E4M3 range after scaling.  Evaluated exactly in double by search. */
+int oracle_ue8m0_exponent(float a)
+{
+    double ad = (double)a;
+    int k = 0;
+    assert(a > 0.0f);
+    while (ad > ldexp(448.0, k))
+        k++;
+    while (ad <= ldexp(448.0, k - 1))
+        k--;
+    return k;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Layout: counts, offsets, stable slots, source-index maps                 */
+/* ------------------------------------------------------------------------ */
+
+enum { ORACLE_CONTIGUOUS = 0, ORACLE_MASKED = 1 };
+
+/*
+ * Pairs p = t*K + k are visited in ascending p.  e = topk_idx[p]:
+ *   0 <= e < E  routed;  e == -1 unrouted (skipped);  anything else invalid
+ *   (skipped and counted in status[1]).
+ * count[e]  = number of routed pairs with expert e.
+ * slot(p)   = number of routed pairs q < p with the same expert (a stable
+ *             counting sort: rows of one expert keep ascending pair order).
+ * Contiguous: segment of e starts at expert_offset[e], segments are padded to
+ *             a multiple of `align` rows; row(p) = expert_offset[e] + slot(p).
+ * Masked:     expert e owns rows [e*C, (e+1)*C); row(p) = e*C + slot(p) when
+ *             slot(p) < C, otherwise the pair is dropped and counted in
+ *             status[0]; recv_count[e] = min(count[e], C).
+ * rank_offset[r] = expert_offset[r * E/R]: virtual rank r owns experts
+ *             [r*E/R, (r+1)*E/R), which are rows rank_offset[r]..[r+1].
+ * pair_to_row[p] = row(p) or -1; row_to_pair[row] = p for kept pairs and -1
+ *             for every other row in [0, rows_capacity).
+ * Returns 0, or -1 if the rows needed exceed rows_capacity.
+ */
+int oracle_dispatch_layout(int32_t T, int32_t K, int32_t E, int32_t R,
+                           int32_t layout, int32_t align, int32_t capacity,
+                           int64_t rows_capacity, const int32_t *topk_idx,
+                           int32_t *expert_count, int32_t *recv_count,
+                           int32_t *expert_offset, int32_t *rank_offset,
+                           int32_t *pair_to_row, int32_t *row_to_pair,
+                           int32_t *status)
+{
+    int64_t P = (int64_t)T * K;
+    int32_t L = E / R;
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    assert(seen != NULL);
+
+    status[0] = 0;
+    status[1] = 0;
+    for (int32_t e = 0; e < E; e++)
+        expert_count[e] = 0;
+
+    /* counts */
+    for (int64_t p = 0; p < P; p++) {
+        int32_t e = topk_idx[p];
+        if (e >= 0 && e < E)
+            expert_count[e]++;
+        else if (e != -1)
+            status[1]++;
+    }
+
+    /* segment offsets */
+    expert_offset[0] = 0;
+    for (int32_t e = 0; e < E; e++) {
+        if (layout == ORACLE_CONTIGUOUS) {
+            int32_t padded = ((expert_count[e] + align - 1) / align) * align;
+            expert_offset[e + 1] = expert_offset[e] + padded;
+            recv_count[e] = expert_count[e];
+        } else {
+            expert_offset[e + 1] = (e + 1) * capacity;
+            recv_count[e] = expert_count[e] < capacity ? expert_count[e] : capacity;
+            if (expert_count[e] > capacity)
+                status[0] += expert_count[e] - capacity;
+        }
+    }
+    for (int32_t r = 0; r <= R; r++)
+        rank_offset[r] = expert_offset[r * L];
+
+    if ((int64_t)expert_offset[E] > rows_capacity) {
+        free(seen);
+        return -1;
+    }
+
+    for (int64_t row = 0; row < rows_capacity; row++)
+        row_to_pair[row] = -1;
+
+    /* stable slots and both maps */
+    for (int64_t p = 0; p < P; p++) {
+        int32_t e = topk_idx[p];
+        if (!(e >= 0 && e < E)) {
+            pair_to_row[p] = -1;
+            continue;
+        }
+        int32_t slot = seen[e]++;
+        int32_t row;
+        if (layout == ORACLE_CONTIGUOUS)
+            row = expert_offset[e] + slot;
+        else
+            row = slot < capacity ? e * capacity + slot : -1;
+        pair_to_row[p] = row;
+        if (row >= 0)
+            row_to_pair[row] = (int32_t)p;
+    }
+    free(seen);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch: row permutation, optional fused FP8 1x128 quantization          */
+/* ------------------------------------------------------------------------ */
+
+enum { ORACLE_QUANT_NONE = 0, ORACLE_QUANT_FP8_F32 = 1, ORACLE_QUANT_FP8_UE8M0 = 2 };
+
+#define ORACLE_BLOCK 128          /* activation quantization group, 1 x 128 */
+#define ORACLE_AMAX_FLOOR 1e-10f  /* keeps the scale of an all-zero block finite */
+
+/* Quantize one token row (H channels) into E4M3 bytes `q` and its per-block
+ * scales.  For block b (channels 128b .. 128b+127):
+ *   amax = max |x|, a = max(amax, 1e-10)
+ *   fp32 scales : s = a / 448 (binary32 division), q = E4M3(clamp(x / s, +-448))
+ *   UE8M0 scales: k = smallest integer with a <= 448 * 2^k, scale byte k + 127,
+ *                 q = E4M3(x * 2^-k)  (exact scaling; the clamp cannot bind)
+ * Scales go to s32[b] (fp32) or byte b of the packed little-endian words w32
+ * (four blocks per word, unused high bytes zero). */
+static void quantize_token_row(int32_t H, int32_t quant, const uint16_t *x,
+                               uint8_t *q, float *s32, uint32_t *w32)
+{
+    int32_t NB = H / ORACLE_BLOCK;
+    if (quant == ORACLE_QUANT_FP8_UE8M0)
+        for (int32_t w = 0; w < (NB + 3) / 4; w++)
+            w32[w] = 0;
+    for (int32_t b = 0; b < NB; b++) {
+        const uint16_t *xb = x + (int64_t)b * ORACLE_BLOCK;
+        float amax = 0.0f;
+        for (int j = 0; j < ORACLE_BLOCK; j++) {
+            float v = fabsf(oracle_bf16_to_float(xb[j]));
+            assert(isfinite(v));
+            if (v > amax)
+                amax = v;
+        }
+        float a = amax > ORACLE_AMAX_FLOOR ? amax : ORACLE_AMAX_FLOOR;
+        if (quant == ORACLE_QUANT_FP8_F32) {
+            float s = a / 448.0f;
+            s32[b] = s;
+            for (int j = 0; j < ORACLE_BLOCK; j++) {
+                float v = oracle_bf16_to_float(xb[j]) / s;
+                if (v > 448.0f)
+                    v = 448.0f;
+                if (v < -448.0f)
+                    v = -448.0f;
+                q[(int64_t)b * ORACLE_BLOCK + j] = oracle_e4m3_encode(v);
+            }
+        } else {
+            int k = oracle_ue8m0_exponent(a);
+            assert(k + 127 >= 0 && k + 127 <= 254);
+            w32[b / 4] |= (uint32_t)(k + 127) << (8 * (b % 4));
+            for (int j = 0; j < ORACLE_BLOCK; j++) {
+                float v = ldexpf(oracle_bf16_to_float(xb[j]), -k);
+                q[(int64_t)b * ORACLE_BLOCK + j] = oracle_e4m3_encode(v);
+            }
+        }
+    }
+}
+
+/*
+ * For every kept pair p (pair_to_row[p] >= 0) of token t = p / K:
+ *   quant NONE : out_x[row, :] = x[t, :]           (bf16 bit copy, H*2 bytes)
+ *   quant FP8  : out_x[row, :] = E4M3 bytes of x[t, :] (H bytes) and the
+ *                row's scales in out_scale (fp32 [rows, H/128] or packed
+ *                UE8M0 uint32 [rows, ceil(H/512)]).
+ *   out_row_weight[row] = topk_w[p] when both pointers are given.
+ * Quantization happens once per token; every kept row of the token receives
+ * the same bytes.  Rows that no kept pair maps to are not written.
+ */
+void oracle_dispatch(int32_t T, int32_t K, int32_t H, int32_t quant,
+                     const uint16_t *x, const float *topk_w,
+                     const int32_t *pair_to_row, void *out_x, void *out_scale,
+                     float *out_row_weight)
+{
+    int32_t NB = H / ORACLE_BLOCK;
+    int32_t NW = (NB + 3) / 4;
+    uint8_t *q = NULL;
+    float *s32 = NULL;
+    uint32_t *w32 = NULL;
+    if (quant != ORACLE_QUANT_NONE) {
+        q = (uint8_t *)malloc((size_t)H);
+        s32 = (float *)malloc(sizeof(float) * (size_t)(NB > 0 ? NB : 1));
+        w32 = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(NW > 0 ? NW : 1));
+        assert(q && s32 && w32);
+    }
+    for (int32_t t = 0; t < T; t++) {
+        const uint16_t *xt = x + (int64_t)t * H;
+        int any = 0;
+        for (int32_t k = 0; k < K; k++)
+            any |= pair_to_row[(int64_t)t * K + k] >= 0;
+        if (!any)
+            continue;
+        if (quant != ORACLE_QUANT_NONE)
+            quantize_token_row(H, quant, xt, q, s32, w32);
+        for (int32_t k = 0; k < K; k++) {
+            int64_t p = (int64_t)t * K + k;
+            int32_t row = pair_to_row[p];
+            if (row < 0)
+                continue;
+            if (quant == ORACLE_QUANT_NONE) {
+                uint16_t *dst = (uint16_t *)out_x + (int64_t)row * H;
+                for (int32_t j = 0; j < H; j++)
+                    dst[j] = xt[j];
+            } else {
+                uint8_t *dst = (uint8_t *)out_x + (int64_t)row * H;
+                for (int32_t j = 0; j < H; j++)
+                    dst[j] = q[j];
+                if (quant == ORACLE_QUANT_FP8_F32) {
+                    float *sd = (float *)out_scale + (int64_t)row * NB;
+                    for (int32_t b = 0; b < NB; b++)
+                        sd[b] = s32[b];
+                } else {
+                    uint32_t *wd = (uint32_t *)out_scale + (int64_t)row * NW;
+                    for (int32_t w = 0; w < NW; w++)
+                        wd[w] = w32[w];
+                }
+            }
+            if (out_row_weight != NULL && topk_w != NULL)
+                out_row_weight[row] = topk_w[p];
+        }
+    }
+    free(q);
+    free(s32);
+    free(w32);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine: router-weighted top-k reduction back to token order             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * out[t, j] = bf16_RNE( sum over k = 0..K-1 with row = pair_to_row[t*K+k] >= 0
+ *                        of topk_w[t*K+k] * y[row, j] )
+ * accumulated in binary32 starting from +0, in ascending k, the product and the
+ * sum each rounded to binary32 (no fused multiply-add).  A token with no kept
+ * pair gives +0.  The weights are the caller's router weights as given (no
+ * renormalisation over kept pairs), and nothing is reduced afterwards.
+ */
+void oracle_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y,
+                    const float *topk_w, const int32_t *pair_to_row,
+                    uint16_t *out)
+{
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t j = 0; j < H; j++) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; k++) {
+                int64_t p = (int64_t)t * K + k;
+                int32_t row = pair_to_row[p];
+                if (row < 0)
+                    continue;
+                float prod = topk_w[p] * oracle_bf16_to_float(y[(int64_t)row * H + j]);
+                acc = acc + prod;
+            }
+            out[(int64_t)t * H + j] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Array forms of the codecs, so the tests can sweep them in bulk           */
+/* ------------------------------------------------------------------------ */
+
+void oracle_bf16_rne_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_bf16_rne(in[i]);
+}
+
+void oracle_e4m3_encode_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_e4m3_encode(in[i]);
+}
+
+void oracle_ue8m0_exponent_array(const float *in, int32_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_ue8m0_exponent(in[i]);
+}
