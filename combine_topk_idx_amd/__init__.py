@@ -1,0 +1,254 @@
+"""MI355X (gfx950) MoE token dispatch / combine.
+
+A thin ctypes binding over ``libmoe_dispatch.so`` (HIP kernels behind the C
+ABI declared in ``include/moe_dispatch.h``).  The Python functions carry the
+same names as the C entry points and only marshal arguments: torch tensors
+supply device memory and the current HIP stream, and every step of the path
+runs in the library's kernels.  There is no fallback: if the library is not
+built, or the process has no GPU, the calls raise.
+
+Typical use (prefill, FP8 with UE8M0 scales)::
+
+    cfg = MoeConfig(max_tokens=8192, hidden=7168, num_experts=256, num_topk=8,
+                    num_ranks=8, layout=LAYOUT_CONTIGUOUS, align=128,
+                    quant=QUANT_FP8_UE8M0)
+    bufs = DispatchBuffers(cfg, device="cuda")
+    moe_dispatch_layout(cfg, T, topk_idx, bufs.handle, bufs.workspace)
+    moe_dispatch(cfg, T, x, None, bufs.handle, bufs.out_x, bufs.out_scale)
+    ...  # experts write y in the dispatched layout
+    moe_combine(cfg, T, y, topk_w, bufs.handle, out)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_dispatch.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_CAPACITY = 2
+MOE_ERR_UNSUPPORTED = 3
+MOE_ERR_HIP = 4
+
+LAYOUT_CONTIGUOUS = 0
+LAYOUT_MASKED = 1
+QUANT_NONE = 0
+QUANT_FP8_F32 = 1
+QUANT_FP8_UE8M0 = 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {moe_status_str(code)} ({code})")
+        self.code = code
+
+
+class MoeConfig(ctypes.Structure):
+    """moe_config_t."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "max_tokens", "hidden", "num_experts", "num_topk", "num_ranks",
+        "layout", "align", "capacity", "quant", "num_cus")]
+
+    def __init__(self, max_tokens, hidden, num_experts, num_topk, num_ranks,
+                 layout=LAYOUT_CONTIGUOUS, align=1, capacity=1, quant=QUANT_NONE, num_cus=0):
+        super().__init__(max_tokens, hidden, num_experts, num_topk, num_ranks,
+                         layout, align, capacity, quant, num_cus)
+
+
+class MoeHandle(ctypes.Structure):
+    """moe_handle_t: device pointers of the handle arrays."""
+
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "expert_count", "recv_count", "expert_offset", "rank_offset",
+        "pair_to_row", "row_to_pair", "status")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m combine_topk_idx_amd.build` "
+            "(hipcc, gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp, hp = ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeHandle)
+    lib.moe_rows_capacity.argtypes = [cfgp]
+    lib.moe_rows_capacity.restype = sz
+    lib.moe_workspace_bytes.argtypes = [cfgp]
+    lib.moe_workspace_bytes.restype = sz
+    lib.moe_config_check.argtypes = [cfgp]
+    lib.moe_config_check.restype = ctypes.c_int
+    lib.moe_dispatch_layout.argtypes = [cfgp, i32, P, hp, P, sz, P]
+    lib.moe_dispatch_layout.restype = ctypes.c_int
+    lib.moe_dispatch.argtypes = [cfgp, i32, P, P, hp, P, P, P, P]
+    lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_combine.argtypes = [cfgp, i32, P, P, hp, P, P]
+    lib.moe_combine.restype = ctypes.c_int
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libmoe_dispatch.so (raises if it is not built)."""
+    return _load()
+
+
+def moe_status_str(code: int) -> str:
+    return _load().moe_status_str(code).decode()
+
+
+def moe_rows_capacity(cfg: MoeConfig) -> int:
+    return int(_load().moe_rows_capacity(ctypes.byref(cfg)))
+
+
+def moe_workspace_bytes(cfg: MoeConfig) -> int:
+    return int(_load().moe_workspace_bytes(ctypes.byref(cfg)))
+
+
+def moe_config_check(cfg: MoeConfig) -> int:
+    return int(_load().moe_config_check(ctypes.byref(cfg)))
+
+
+# ---- marshalling helpers ----------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor], dtype_bytes: Optional[int] = None,
+         min_elems: int = 0, name: str = "") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype_bytes is not None and t.element_size() != dtype_bytes:
+        raise ValueError(f"{name}: expected {dtype_bytes}-byte elements, got {t.dtype}")
+    if t.numel() < min_elems:
+        raise ValueError(f"{name}: {t.numel()} elements < required {min_elems}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, code: int):
+    if code != MOE_OK:
+        raise MoeError(fn, code)
+
+
+class Handle:
+    """Device arrays of one dispatch handle (moe_handle_t), allocated by torch."""
+
+    def __init__(self, cfg: MoeConfig, device="cuda"):
+        E, R = cfg.num_experts, cfg.num_ranks
+        rows = moe_rows_capacity(cfg)
+        if rows == 0 and moe_config_check(cfg) != MOE_OK:
+            raise MoeError("moe_rows_capacity", moe_config_check(cfg))
+        z = lambda n: torch.empty(max(int(n), 1), dtype=torch.int32, device=device)
+        self.expert_count = z(E)
+        self.recv_count = z(E)
+        self.expert_offset = z(E + 1)
+        self.rank_offset = z(R + 1)
+        self.pair_to_row = z(cfg.max_tokens * cfg.num_topk)
+        self.row_to_pair = z(rows)
+        self.status = z(2)
+        self.c = MoeHandle(*(t.data_ptr() for t in (
+            self.expert_count, self.recv_count, self.expert_offset, self.rank_offset,
+            self.pair_to_row, self.row_to_pair, self.status)))
+
+    def tensors(self) -> dict:
+        return {k: getattr(self, k) for k in (
+            "expert_count", "recv_count", "expert_offset", "rank_offset",
+            "pair_to_row", "row_to_pair", "status")}
+
+
+class DispatchBuffers:
+    """Handle, workspace and dispatched-activation buffers sized for a config."""
+
+    def __init__(self, cfg: MoeConfig, device="cuda", row_weight: bool = False):
+        self.cfg = cfg
+        self.rows = moe_rows_capacity(cfg)
+        self.handle = Handle(cfg, device)
+        self.workspace = torch.empty(max(moe_workspace_bytes(cfg), 4), dtype=torch.uint8, device=device)
+        H = cfg.hidden
+        if cfg.quant == QUANT_NONE:
+            self.out_x = torch.empty((self.rows, H), dtype=torch.int16, device=device)
+            self.out_scale = None
+        else:
+            self.out_x = torch.empty((self.rows, H), dtype=torch.uint8, device=device)
+            nb = H // 128
+            if cfg.quant == QUANT_FP8_F32:
+                self.out_scale = torch.empty((self.rows, nb), dtype=torch.float32, device=device)
+            else:
+                self.out_scale = torch.empty((self.rows, (nb + 3) // 4), dtype=torch.int32, device=device)
+        self.out_row_weight = (torch.empty(self.rows, dtype=torch.float32, device=device)
+                               if row_weight else None)
+
+
+# ---- entry points -----------------------------------------------------------
+
+def moe_dispatch_layout(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, handle: Handle,
+                        workspace: torch.Tensor, stream=None) -> None:
+    """Counts, offsets, stable slots and both maps from int32 topk_idx [T, K]."""
+    lib = _load()
+    K = cfg.num_topk
+    idx = _ptr(topk_idx, 4, num_tokens * K, "topk_idx") if num_tokens > 0 else None
+    ws = _ptr(workspace, None, 0, "workspace")
+    _check("moe_dispatch_layout", lib.moe_dispatch_layout(
+        ctypes.byref(cfg), int(num_tokens), idx, ctypes.byref(handle.c), ws,
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_dispatch(cfg: MoeConfig, num_tokens: int, x: torch.Tensor, topk_w: Optional[torch.Tensor],
+                 handle: Handle, out_x: torch.Tensor, out_scale: Optional[torch.Tensor] = None,
+                 out_row_weight: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Permute (and FP8-quantize when cfg.quant says so) bf16 rows x [T, H]."""
+    lib = _load()
+    rows = moe_rows_capacity(cfg)
+    H, K = cfg.hidden, cfg.num_topk
+    nb = H // 128
+    xp = _ptr(x, 2, num_tokens * H, "x") if num_tokens > 0 else None
+    wp = _ptr(topk_w, 4, num_tokens * K if out_row_weight is not None else 0, "topk_w")
+    ob = 2 if cfg.quant == QUANT_NONE else 1
+    op = _ptr(out_x, None, rows * H * ob // out_x.element_size(), "out_x")
+    sp = None
+    if cfg.quant == QUANT_FP8_F32:
+        sp = _ptr(out_scale, 4, rows * nb, "out_scale")
+    elif cfg.quant == QUANT_FP8_UE8M0:
+        sp = _ptr(out_scale, 4, rows * ((nb + 3) // 4), "out_scale")
+    elif out_scale is not None:
+        raise ValueError("out_scale must be None without FP8 quantization")
+    rp = _ptr(out_row_weight, 4, rows, "out_row_weight")
+    _check("moe_dispatch", lib.moe_dispatch(
+        ctypes.byref(cfg), int(num_tokens), xp, wp, ctypes.byref(handle.c), op, sp, rp,
+        _stream(stream)))
+
+
+def moe_combine(cfg: MoeConfig, num_tokens: int, y: torch.Tensor, topk_w: torch.Tensor,
+                handle: Handle, out: torch.Tensor, stream=None) -> None:
+    """out[t] = bf16(sum_k w[t,k] * y[row(t,k)]) with fp32 accumulation."""
+    lib = _load()
+    rows = moe_rows_capacity(cfg)
+    H, K = cfg.hidden, cfg.num_topk
+    if num_tokens == 0:
+        yp = wp = op = None
+    else:
+        yp = _ptr(y, 2, rows * H, "y")
+        wp = _ptr(topk_w, 4, num_tokens * K, "topk_w")
+        op = _ptr(out, 2, num_tokens * H, "out")
+    _check("moe_combine", lib.moe_combine(
+        ctypes.byref(cfg), int(num_tokens), yp, wp, ctypes.byref(handle.c), op, _stream(stream)))

@@ -1,0 +1,280 @@
+// C ABI of libmoe_dispatch.so: host-side validation, launch planning, and
+// the extern "C" entry points declared in include/moe_dispatch.h.
+//
+// Every argument error is found here, before anything is enqueued; the
+// library allocates nothing and keeps no state besides a cached compute-unit
+// count per device.
+#include <limits.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t rows_capacity64(const moe_config_t &c)
+{
+    if (c.layout == MOE_LAYOUT_CONTIGUOUS)
+        return (int64_t)c.max_tokens * c.num_topk + (int64_t)c.num_experts * (c.align - 1);
+    return (int64_t)c.num_experts * c.capacity;
+}
+
+moe_status_t check_config(const moe_config_t *cfg)
+{
+    if (cfg == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    const moe_config_t &c = *cfg;
+    if (c.max_tokens < 0 || c.hidden < 8 || c.hidden % 8 != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c.num_experts < 1 || c.num_topk < 1 || c.num_topk > kMaxTopk || c.num_ranks < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (c.num_experts % c.num_ranks != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c.layout != MOE_LAYOUT_CONTIGUOUS && c.layout != MOE_LAYOUT_MASKED)
+        return MOE_ERR_INVALID_ARG;
+    if (c.layout == MOE_LAYOUT_CONTIGUOUS && c.align < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (c.layout == MOE_LAYOUT_MASKED && c.capacity < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (c.quant != MOE_QUANT_NONE && c.quant != MOE_QUANT_FP8_F32 && c.quant != MOE_QUANT_FP8_UE8M0)
+        return MOE_ERR_INVALID_ARG;
+    if (c.quant != MOE_QUANT_NONE && c.hidden % kQuantGroup != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c.num_cus < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c.num_experts > kMaxExperts)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)c.max_tokens * c.num_topk > INT32_MAX || rows_capacity64(c) > INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_handle(const moe_handle_t *h)
+{
+    if (h == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    const int32_t *arr[] = {h->expert_count, h->recv_count, h->expert_offset, h->rank_offset,
+                            h->pair_to_row, h->row_to_pair, h->status};
+    for (const int32_t *p : arr)
+        if (p == nullptr || !aligned(p, 4))
+            return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status_t check_tokens(const moe_config_t &c, int32_t num_tokens)
+{
+    if (num_tokens < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens > c.max_tokens)
+        return MOE_ERR_CAPACITY;
+    return MOE_OK;
+}
+
+int bits_for(int32_t E)
+{
+    int b = 0;
+    while ((1 << b) < E)
+        ++b;
+    return b;
+}
+
+moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Work items: (token, run of iterations).  Each token row has n_iters
+// iterations of `width` columns; a wave keeps at most `max_iters` of them in
+// flight.  Short batches (decode) split rows further so the launch still has
+// several waves per compute unit; num_cus > 0 caps the grid and the waves
+// stride over the items.
+RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters, int32_t num_cus)
+{
+    RowPlan p;
+    p.width = width;
+    p.n_iters = (H + width - 1) / width;
+    const int cus = device_cu_count();
+    const int64_t target_waves = (int64_t)cus * 8;
+    int64_t per_token = (p.n_iters + max_iters - 1) / max_iters;
+    if ((int64_t)T * per_token < target_waves && T > 0) {
+        const int64_t want = (target_waves + T - 1) / T;
+        per_token = want < p.n_iters ? want : p.n_iters;
+    }
+    if (per_token < 1)
+        per_token = 1;
+    p.iters_per_item = (int32_t)((p.n_iters + per_token - 1) / per_token);
+    p.items_per_token = (p.n_iters + p.iters_per_item - 1) / p.iters_per_item;
+    p.n_items = (int64_t)T * p.items_per_token;
+    int64_t grid = (p.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (num_cus > 0) {
+        const int64_t cap = (int64_t)num_cus * 8;  // 8 workgroups (32 waves) per CU
+        if (grid > cap)
+            grid = cap;
+    }
+    p.grid = (int32_t)(grid < 1 ? 1 : grid);
+    return p;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_rows_capacity(const moe_config_t *cfg)
+{
+    if (check_config(cfg) != MOE_OK)
+        return 0;
+    return (size_t)rows_capacity64(*cfg);
+}
+
+size_t moe_workspace_bytes(const moe_config_t *cfg)
+{
+    if (check_config(cfg) != MOE_OK)
+        return 0;
+    const LayoutPlan lp = layout_plan((int64_t)cfg->max_tokens * cfg->num_topk);
+    const size_t bytes = sizeof(int32_t) * (size_t)lp.nblocks * (size_t)(cfg->num_experts + 1);
+    return (bytes + 255) / 256 * 256;
+}
+
+moe_status_t moe_config_check(const moe_config_t *cfg) { return check_config(cfg); }
+
+moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                                 const moe_handle_t *handle, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
+        return st;
+    if ((num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4))) || workspace == nullptr ||
+        !aligned(workspace, 4))
+        return MOE_ERR_INVALID_ARG;
+    const int64_t P = (int64_t)num_tokens * cfg->num_topk;
+    const LayoutPlan lp = layout_plan(P);
+    if (workspace_bytes < sizeof(int32_t) * (size_t)lp.nblocks * (size_t)(cfg->num_experts + 1))
+        return MOE_ERR_CAPACITY;
+
+    LayoutArgs a;
+    a.topk_idx = topk_idx;
+    a.P = P;
+    a.E = cfg->num_experts;
+    a.R = cfg->num_ranks;
+    a.L = cfg->num_experts / cfg->num_ranks;
+    a.layout = cfg->layout;
+    a.align = cfg->layout == MOE_LAYOUT_CONTIGUOUS ? cfg->align : 1;
+    a.capacity = cfg->layout == MOE_LAYOUT_MASKED ? cfg->capacity : 1;
+    a.rows_cap = (int32_t)rows_capacity64(*cfg);
+    a.nbits = bits_for(cfg->num_experts);
+    a.chunk = lp.chunk;
+    a.nblocks = lp.nblocks;
+    a.ws = static_cast<int32_t *>(workspace);
+    a.h = *handle;
+    return from_hip(launch_layout(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x, const float *topk_w,
+                          const moe_handle_t *handle, void *out_x, void *out_scale, float *out_row_weight,
+                          void *stream)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
+        return st;
+    const bool fp8 = cfg->quant != MOE_QUANT_NONE;
+    if (out_x == nullptr || !aligned(out_x, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 ? (out_scale == nullptr || !aligned(out_scale, 4)) : out_scale != nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (out_row_weight != nullptr && !aligned(out_row_weight, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (out_row_weight != nullptr && num_tokens > 0 && (topk_w == nullptr || !aligned(topk_w, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens > 0 && (x == nullptr || !aligned(x, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return MOE_OK;
+
+    DispatchArgs a;
+    a.x = x;
+    a.topk_w = topk_w;
+    a.pair_to_row = handle->pair_to_row;
+    a.out_x = out_x;
+    a.out_scale = out_scale;
+    a.out_row_weight = out_row_weight;
+    a.T = num_tokens;
+    a.K = cfg->num_topk;
+    a.H = cfg->hidden;
+    a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus)
+                 : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus);
+    return from_hip(launch_dispatch(a, cfg->quant, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *y, const float *topk_w,
+                         const moe_handle_t *handle, uint16_t *out, void *stream)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
+        return st;
+    if (num_tokens > 0 && (y == nullptr || !aligned(y, 16) || topk_w == nullptr || !aligned(topk_w, 4) ||
+                           out == nullptr || !aligned(out, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return MOE_OK;
+
+    CombineArgs a;
+    a.y = y;
+    a.topk_w = topk_w;
+    a.pair_to_row = handle->pair_to_row;
+    a.out = out;
+    a.T = num_tokens;
+    a.K = cfg->num_topk;
+    a.H = cfg->hidden;
+    a.plan = row_plan(num_tokens, cfg->hidden, kCombineWidth, kCombineMaxIters, cfg->num_cus);
+    return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+const char *moe_status_str(moe_status_t status)
+{
+    switch (status) {
+    case MOE_OK:
+        return "MOE_OK";
+    case MOE_ERR_INVALID_ARG:
+        return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_CAPACITY:
+        return "MOE_ERR_CAPACITY";
+    case MOE_ERR_UNSUPPORTED:
+        return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP:
+        return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Combine on gfx950: the router-weighted top-k reduction of expert outputs
+// back to token order (page vLLM tools/ep_kernels, commit message: weighted
+// reduction in combine), with nothing reduced afterwards (page "[Feature] Add
+// DeepEPv2 (ElasticBuffer) MoE A2A backend", review: an extra post-expert
+// reduction double-counts).
+//
+// Token-major: a wave owns a token (or a run of its columns).  The token's
+// kept rows and weights are compacted once into lanes 0..n-1 (ds_permute),
+// then every 512-column iteration issues one 16-byte load per kept row (up to
+// 8 in flight per lane), accumulates in ascending k in fp32 with the product
+// and the sum each rounded (no FMA), and stores 8 bf16 (round to nearest even,
+// v_cvt_pk_bf16_f32) as one 16-byte vector.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBatch = 8;  // kept rows whose loads are in flight together
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    const __bf16 ha = (__bf16)a, hb = (__bf16)b;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+#pragma clang fp contract(off)
+__device__ __forceinline__ void accumulate(float (&acc)[8], float w, const uint4 &v)
+{
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(u[j] << 16);
+        const float hi = __uint_as_float(u[j] & 0xFFFF0000u);
+        const float plo = w * lo;
+        const float phi = w * hi;
+        acc[2 * j] = acc[2 * j] + plo;
+        acc[2 * j + 1] = acc[2 * j + 1] + phi;
+    }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const RowPlan &pl = a.plan;
+    for (int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wave; item < pl.n_items;
+         item += (int64_t)gridDim.x * kWavesPerBlock) {
+        const int t = (int)(item / pl.items_per_token);
+        const int c = (int)(item - (int64_t)t * pl.items_per_token);
+
+        // kept rows of the token, compacted in ascending k into lanes 0..n-1
+        const int64_t pbase = (int64_t)t * a.K;
+        const int32_t r = lane < a.K ? a.pair_to_row[pbase + lane] : -1;
+        const float w = lane < a.K ? a.topk_w[pbase + lane] : 0.0f;
+        const uint64_t kept = __ballot(r >= 0);
+        const int n = __popcll(kept);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(kept >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)kept, 0u));
+        // kept lanes go to slot `below`; the others park in lanes 32.. (unused)
+        const int dst = r >= 0 ? below : kMaxTopk + (lane & (kMaxTopk - 1));
+        const int32_t rows = __builtin_amdgcn_ds_permute(dst * 4, r);
+        const float wts = __int_as_float(__builtin_amdgcn_ds_permute(dst * 4, __float_as_int(w)));
+
+        const int it0 = c * pl.iters_per_item;
+        const int it1 = min(it0 + pl.iters_per_item, pl.n_iters);
+        uint16_t *outp = a.out + (int64_t)t * a.H;
+        for (int it = it0; it < it1; ++it) {
+            const int col = it * kCombineWidth + lane * 8;
+            const bool active = col < a.H;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int j0 = 0; j0 < n; j0 += kBatch) {
+                uint4 v[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    if (j0 + j < n) {
+                        const int32_t row = __builtin_amdgcn_readlane(rows, j0 + j);
+                        if (active)
+                            v[j] = *reinterpret_cast<const uint4 *>(a.y + (int64_t)row * a.H + col);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    if (j0 + j < n) {
+                        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                        __float_as_int(wts), j0 + j));
+                        if (active)
+                            accumulate(acc, wj, v[j]);
+                    }
+                }
+            }
+            if (active) {
+                uint4 o;
+                o.x = pack_bf16(acc[0], acc[1]);
+                o.y = pack_bf16(acc[2], acc[3]);
+                o.z = pack_bf16(acc[4], acc[5]);
+                o.w = pack_bf16(acc[6], acc[7]);
+                *reinterpret_cast<uint4 *>(outp + col) = o;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(combine_kernel, dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+// Internal declarations shared by the HIP translation units of
+// libmoe_dispatch.so.  Not part of the public ABI (include/moe_dispatch.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_dispatch.h"
+
+namespace moe {
+
+constexpr int kWave = 64;             // CDNA wavefront width
+constexpr int kBlockThreads = 256;    // 4 waves per workgroup for every kernel
+constexpr int kWavesPerBlock = kBlockThreads / kWave;
+constexpr int kQuantGroup = 128;      // 1x128 activation quantization group
+constexpr int kMaxTopk = 32;
+constexpr int kMaxExperts = 2048;     // layout keeps 7 int32 per expert in LDS
+constexpr int kLayoutMaxBlocks = 64;  // cap on layout workgroups (bounds the workspace)
+constexpr int kLayoutChunkUnit = 1024;
+
+// ---- layout ---------------------------------------------------------------
+
+struct LayoutArgs {
+    const int32_t *topk_idx;
+    int64_t P;          // pairs = num_tokens * K
+    int32_t E, R, L;    // experts, ranks, experts per rank
+    int32_t layout, align, capacity;
+    int32_t rows_cap;   // rows of row_to_pair
+    int32_t nbits;      // bits needed to tell experts apart (ballot match)
+    int32_t chunk;      // pairs per workgroup, multiple of 4 * 64
+    int32_t nblocks;    // workgroups = ceil(P / chunk), >= 1
+    int32_t *ws;        // [nblocks][E + 1] block histograms (+ invalid count)
+    moe_handle_t h;
+};
+
+struct LayoutPlan {
+    int32_t chunk, nblocks;
+};
+LayoutPlan layout_plan(int64_t P);
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+
+// ---- dispatch / combine -----------------------------------------------------
+
+// Work is split into items of (token, run of column iterations); one wave
+// processes one item at a time and walks items with a grid stride.
+struct RowPlan {
+    int32_t width;            // columns per wave iteration
+    int32_t n_iters;          // iterations per row = ceil(H / width)
+    int32_t items_per_token;
+    int32_t iters_per_item;
+    int64_t n_items;
+    int32_t grid;             // workgroups launched
+};
+
+struct DispatchArgs {
+    const uint16_t *x;
+    const float *topk_w;
+    const int32_t *pair_to_row;
+    void *out_x;
+    void *out_scale;
+    float *out_row_weight;
+    int32_t T, K, H;
+    RowPlan plan;
+};
+
+struct CombineArgs {
+    const uint16_t *y;
+    const float *topk_w;
+    const int32_t *pair_to_row;
+    uint16_t *out;
+    int32_t T, K, H;
+    RowPlan plan;
+};
+
+int device_cu_count();
+RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item,
+                 int32_t num_cus);
+hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+// Columns one wave iteration covers, and how many iterations a wave keeps in
+// registers at once, per kernel.
+constexpr int kDispatchBf16Width = kWave * 8;    // 8 bf16 = 16 bytes per lane
+constexpr int kDispatchBf16MaxIters = 16;
+constexpr int kDispatchFp8Width = kWave * 16;    // 16 channels per lane, 8 lanes per block
+constexpr int kDispatchFp8MaxIters = 8;
+constexpr int kCombineWidth = kWave * 8;         // 8 bf16 per lane
+constexpr int kCombineMaxIters = 64;
+
+}  // namespace moe

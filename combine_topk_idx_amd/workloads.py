@@ -206,16 +206,23 @@ def expert_outputs(wl: Workload, inp: Inputs, row_to_pair: Optional[np.ndarray] 
                    rows: Optional[int] = None) -> np.ndarray:
     """Stand-in expert outputs y, bf16 bits [rows, H], in the dispatched layout.
 
-    "random": every row ~ N(0,1) (layout independent; rows defaults to the
-    workload's rows_capacity).
+    "random": every row is a window of H consecutive values of a seeded
+    N(0,1) bf16 pool (2^22 values) at a seeded random offset, so rows differ
+    and generation stays fast at full size (layout independent; rows
+    defaults to the workload's rows_capacity).
     "scaled": row r holding pair p = row_to_pair[r] of token t = p // K routed
     to expert e gets bf16((e + 1) * 0.5 * x[t]); rows holding no pair are 0.
     This needs the layout's row_to_pair map.
     """
     n = wl.rows_capacity if rows is None else rows
     if wl.expert_output == "random":
-        y = inp.rng.standard_normal((n, wl.H), dtype=np.float32)
-        return f32_to_bf16_bits(y)
+        pool_n = 1 << 22
+        pool = f32_to_bf16_bits(inp.rng.standard_normal(pool_n + wl.H, dtype=np.float32))
+        offs = inp.rng.integers(0, pool_n, n)
+        y = np.empty((n, wl.H), np.uint16)
+        for r in range(n):
+            y[r] = pool[offs[r]:offs[r] + wl.H]
+        return y
     if wl.expert_output == "scaled":
         if row_to_pair is None:
             raise ValueError("scaled expert outputs need row_to_pair")

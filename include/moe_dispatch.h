@@ -1,0 +1,200 @@
+/*
+ * moe_dispatch.h -- C ABI of the MI355X (gfx950) MoE token dispatch / combine
+ * library (libmoe_dispatch.so).
+ *
+ * The library computes, on one GPU, the data-parallel part of an
+ * expert-parallel MoE layer's token exchange: from router top-k expert ids it
+ * builds the dispatch layout, permutes (optionally FP8-quantizes) token rows
+ * into that layout, and reduces expert outputs back to token order with the
+ * router weights.  Destination ranks are virtual: rank r owns the contiguous
+ * row range [rank_offset[r], rank_offset[r+1]) of the device buffers, which is
+ * what a real expert-parallel exchange would send to rank r.  There is no
+ * transfer between GPUs.
+ *
+ * Pages cited below by title and section:
+ *   [V2-PR]  "moe: add DeepEP V2 ElasticBuffer support to MoE token dispatcher"
+ *   [A2A]    "[Feature] Add DeepEPv2 (ElasticBuffer) MoE A2A backend"
+ *   [DISC]   "deepep v2 support?"
+ *   [VLLM]   vLLM tools/ep_kernels, commit "Add a new deepep_v2 all2all backend"
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, caller-allocated and
+ *     caller-owned; the library never allocates, frees or synchronizes, and
+ *     keeps no state between calls (calls are reentrant).
+ *   - Arrays are dense and row-major.  Activation / output base pointers must
+ *     be 16-byte aligned, int32 / float arrays 4-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without waiting.
+ *   - Argument errors are detected on the host and returned BEFORE anything
+ *     is enqueued.  Data errors (invalid expert ids, masked-capacity overflow)
+ *     are not errors: they are counted on the device in handle.status.
+ *   - A launch failure returns MOE_ERR_HIP (hipGetLastError after launch).
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* bad config value, null or misaligned pointer, bad enum */
+    MOE_ERR_CAPACITY = 2,    /* num_tokens > max_tokens, or a buffer smaller than required */
+    MOE_ERR_UNSUPPORTED = 3, /* a valid but unsupported shape (e.g. too many experts) */
+    MOE_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} moe_status_t;
+
+/* Dispatched layout.  Prefill (extend) uses the per-expert-contiguous
+ * "expanded" layout, decode the fixed-capacity masked slab, independently of
+ * the communication topology ([A2A] Supported scope, layouts paragraph; [A2A]
+ * review reply on layout following the inference phase; [VLLM] commit
+ * message, do_expand). */
+typedef enum {
+    MOE_LAYOUT_CONTIGUOUS = 0, /* expert segments back to back, each padded to `align` rows */
+    MOE_LAYOUT_MASKED = 1      /* [experts, capacity] rows, slot s of expert e = row e*capacity+s */
+} moe_layout_t;
+
+/* Dispatched activation format.  FP8 activations with dynamic per-token
+ * 1x128 scales feed 128x128 block-FP8 expert GEMMs; scales are fp32 for
+ * Hopper-style consumers or packed UE8M0 powers of two for Blackwell-style
+ * consumers ([A2A] Supported scope and Implementation; [DISC] quantization
+ * requirement). */
+typedef enum {
+    MOE_QUANT_NONE = 0,      /* bf16 rows, bit copies of the input */
+    MOE_QUANT_FP8_F32 = 1,   /* E4M3 rows + fp32 scale per 128 channels */
+    MOE_QUANT_FP8_UE8M0 = 2  /* E4M3 rows + one exponent byte per 128 channels, 4 per uint32 */
+} moe_quant_t;
+
+/* Problem shape, fixed for the lifetime of the buffers sized from it.
+ * The buffer is sized from the per-rank token cap, hidden size and the real
+ * top-k ([V2-PR] Motivation and the num_topk review commit: sizing for a
+ * top-k of 32 instead of the model's 8 oversizes memory about 4x); the token
+ * cap lives only here, never per call, because a per-call value that silently
+ * overrides it is a known pitfall ([V2-PR] Modifications, sizing item). */
+typedef struct {
+    int32_t max_tokens;  /* per-call token cap (>= 0); num_tokens > max_tokens -> MOE_ERR_CAPACITY */
+    int32_t hidden;      /* H: channels per token, multiple of 8 (of 128 with FP8) */
+    int32_t num_experts; /* E: routed experts, 1..4096 */
+    int32_t num_topk;    /* K: experts per token, 1..32 ([V2-PR] top-k thread: kNumTopk <= 32) */
+    int32_t num_ranks;   /* R: virtual destination ranks, E % R == 0; rank r owns experts [r*E/R, (r+1)*E/R) */
+    int32_t layout;      /* moe_layout_t */
+    int32_t align;       /* contiguous: segment alignment in rows, >= 1 (ignored when masked) */
+    int32_t capacity;    /* masked: rows per expert, >= 1 (ignored when contiguous) */
+    int32_t quant;       /* moe_quant_t */
+    int32_t num_cus;     /* compute units the data kernels may occupy; 0 = all ([A2A] review: 0 = automatic) */
+} moe_config_t;
+
+/* The dispatch handle: caller-allocated int32 device arrays, written by
+ * moe_dispatch_layout and read by moe_dispatch and moe_combine.  It carries
+ * the per-expert received counts and the source-index map that combine needs
+ * ([V2-PR] Motivation: counts live on the handle; combine reuses the dispatch
+ * handle).  It is plain data: valid until the caller overwrites it, and
+ * combine must be given the handle of the dispatch that produced y's layout
+ * ([A2A] Implementation: handles are single-use). */
+typedef struct {
+    int32_t *expert_count;  /* [E]     routed pairs per expert (before any capacity limit) */
+    int32_t *recv_count;    /* [E]     rows written per expert: count (contiguous), min(count, C) (masked) */
+    int32_t *expert_offset; /* [E+1]   first row of expert e; [E] = rows used (contiguous) or E*C (masked) */
+    int32_t *rank_offset;   /* [R+1]   rank_offset[r] = expert_offset[r*E/R] */
+    int32_t *pair_to_row;   /* [max_tokens*K] row of pair p = t*K+k, or -1 (unrouted, invalid, dropped) */
+    int32_t *row_to_pair;   /* [moe_rows_capacity] pair held by each row, or -1; written in full */
+    int32_t *status;        /* [2]     {pairs dropped by masked capacity, invalid expert ids} */
+} moe_handle_t;
+
+/* Rows the dispatched buffers (out_x, out_scale, out_row_weight, y) and
+ * handle.row_to_pair must hold: max_tokens*K + E*(align-1) for the contiguous
+ * layout (every segment may carry up to align-1 padding rows), E*capacity for
+ * the masked layout.  Returns 0 for an invalid config. */
+size_t moe_rows_capacity(const moe_config_t *cfg);
+
+/* Bytes of device workspace moe_dispatch_layout needs (block histograms).
+ * Returns 0 for an invalid config. */
+size_t moe_workspace_bytes(const moe_config_t *cfg);
+
+/* MOE_OK if the config is valid and supported, else the error code. */
+moe_status_t moe_config_check(const moe_config_t *cfg);
+
+/*
+ * Layout: infer the dispatch layout from the router's top-k ids ([V2-PR]
+ * Motivation and the _dispatch_core commit: V2 derives the layout from
+ * topk_idx, with no separate layout pre-pass at the call site).
+ *
+ *   topk_idx   int32 [num_tokens, K]: expert of pair p = t*K+k.  -1 means
+ *              unrouted (skipped); any other id outside [0,E) is invalid
+ *              (skipped, counted in status[1]).
+ *   handle     every array is written: counts, offsets, both maps, status.
+ *   workspace  >= moe_workspace_bytes(cfg) bytes of scratch device memory,
+ *              clobbered; workspace_bytes is its size.
+ *
+ * Rows of one expert hold its pairs in ascending pair order (a stable
+ * counting sort).  Contiguous: row(p) = expert_offset[e] + slot(p), segments
+ * padded to `align`.  Masked: row(p) = e*C + slot(p) if slot(p) < C, else the
+ * pair is dropped (pair_to_row = -1) and counted in status[0].  Rows holding
+ * no pair get row_to_pair = -1.  num_tokens == 0 is a valid call.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY (num_tokens > max_tokens,
+ * workspace too small), MOE_ERR_HIP.
+ */
+moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens,
+                                 const int32_t *topk_idx, const moe_handle_t *handle,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dispatch: move token rows into the layout built by moe_dispatch_layout
+ * (recv_x of [V2-PR] Motivation), quantizing them to FP8 on the way when
+ * cfg.quant asks for it ([A2A] Implementation; [VLLM] commit: FP8
+ * block-quantized dispatch).
+ *
+ *   x               bf16 bits [num_tokens, H].
+ *   topk_w          fp32 [num_tokens, K]; read only when out_row_weight != NULL.
+ *   out_x           [rows_capacity, H]: bf16 (quant NONE) or E4M3 bytes.
+ *   out_scale       quant FP8_F32: fp32 [rows_capacity, H/128];
+ *                   quant FP8_UE8M0: uint32 [rows_capacity, ceil(H/512)], byte
+ *                   b%4 of word b/4 = k_b + 127 where 2^k_b is block b's scale,
+ *                   unused high bytes 0; must be NULL for quant NONE.
+ *   out_row_weight  optional fp32 [rows_capacity]: router weight of the pair in
+ *                   each written row (recv_topk_weights); NULL to skip.
+ *
+ * Per token t and 128-channel block b: amax = max|x|, a = max(amax, 1e-10);
+ * fp32 scales: s = a/448 and q = E4M3(clamp(x/s, -448, 448)); UE8M0: k =
+ * smallest integer with a <= 448*2^k and q = E4M3(x*2^-k).  E4M3 is the OCP
+ * format (max 448), round to nearest even, sign kept.  Each token is read and
+ * quantized once and its bytes stored to all of its kept rows.  Rows that no
+ * kept pair maps to (padding, empty masked slots, dropped pairs) are NOT
+ * written, in out_x, out_scale and out_row_weight alike.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_HIP.
+ */
+moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x,
+                          const float *topk_w, const moe_handle_t *handle, void *out_x,
+                          void *out_scale, float *out_row_weight, void *stream);
+
+/*
+ * Combine: reduce expert outputs back to token order with the router weights
+ * ([VLLM] commit: weighted reduction in combine; [A2A] review: nothing may
+ * reduce again afterwards, an extra post-expert reduction double-counts).
+ *
+ *   y       bf16 bits [rows_capacity, H]: expert outputs in the dispatched layout.
+ *   topk_w  fp32 [num_tokens, K]: the router weights as given (no
+ *           renormalisation over kept pairs).
+ *   out     bf16 bits [num_tokens, H].
+ *
+ * out[t,:] = bf16_RNE( sum over k ascending with row = pair_to_row[t*K+k] >= 0
+ * of topk_w[t*K+k] * y[row,:] ), accumulated in fp32 from +0 with the product
+ * and the sum each rounded to fp32.  A token with no kept pair gives +0.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_HIP.
+ */
+moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *y,
+                         const float *topk_w, const moe_handle_t *handle, uint16_t *out,
+                         void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_H */

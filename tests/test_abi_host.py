@@ -1,0 +1,179 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library is loaded with ctypes and called only in ways that are decided
+on the host before any HIP call: every argument error, the size queries, and
+zero-token dispatch/combine (valid no-ops).  Pointers here are fake aligned
+addresses; the library must reject or accept them without touching them.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_topk_idx_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        pytest.fail("libmoe_dispatch.so is not built (python -m combine_topk_idx_amd.build)")
+    return M.library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == {"moe_rows_capacity", "moe_workspace_bytes", "moe_config_check",
+                          "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_status_str"}
+    out = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def _cfg(**kw):
+    base = dict(max_tokens=64, hidden=256, num_experts=8, num_topk=2, num_ranks=2,
+                layout=M.LAYOUT_CONTIGUOUS, align=1, capacity=1, quant=M.QUANT_NONE, num_cus=0)
+    base.update(kw)
+    return M.MoeConfig(**base)
+
+
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def _handle(**override):
+    vals = {n: FAKE + 0x1000 * i for i, (n, _) in enumerate(M.MoeHandle._fields_)}
+    vals.update(override)
+    return M.MoeHandle(**vals)
+
+
+def test_status_strings(lib):
+    assert M.moe_status_str(0) == "MOE_OK"
+    assert M.moe_status_str(2) == "MOE_ERR_CAPACITY"
+    assert M.moe_status_str(4) == "MOE_ERR_HIP"
+    assert M.moe_status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_size_queries(lib):
+    c = _cfg(max_tokens=8192, hidden=7168, num_experts=256, num_topk=8, num_ranks=8, align=128,
+             quant=M.QUANT_FP8_UE8M0)
+    assert M.moe_rows_capacity(c) == 8192 * 8 + 256 * 127
+    ws = M.moe_workspace_bytes(c)
+    assert ws >= 64 * 257 * 4 and ws % 256 == 0
+    c = _cfg(layout=M.LAYOUT_MASKED, capacity=256, num_experts=256, num_topk=8, num_ranks=8)
+    assert M.moe_rows_capacity(c) == 256 * 256
+    assert M.moe_rows_capacity(_cfg(num_topk=0)) == 0
+    assert M.moe_workspace_bytes(_cfg(num_ranks=3)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_topk=0), M.MOE_ERR_INVALID_ARG),
+    (dict(num_topk=33), M.MOE_ERR_INVALID_ARG),
+    (dict(num_topk=32), M.MOE_OK),
+    (dict(num_ranks=3), M.MOE_ERR_INVALID_ARG),          # E % R != 0
+    (dict(num_ranks=0), M.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=0), M.MOE_ERR_INVALID_ARG),
+    (dict(hidden=100), M.MOE_ERR_INVALID_ARG),            # H % 8 != 0
+    (dict(hidden=0), M.MOE_ERR_INVALID_ARG),
+    (dict(hidden=264, quant=M.QUANT_FP8_F32), M.MOE_ERR_INVALID_ARG),  # H % 128 != 0
+    (dict(hidden=264), M.MOE_OK),
+    (dict(align=0), M.MOE_ERR_INVALID_ARG),
+    (dict(layout=M.LAYOUT_MASKED, capacity=0), M.MOE_ERR_INVALID_ARG),
+    (dict(layout=M.LAYOUT_MASKED, capacity=0, align=0), M.MOE_ERR_INVALID_ARG),
+    (dict(layout=M.LAYOUT_MASKED, capacity=5, align=0), M.MOE_OK),  # align unused
+    (dict(layout=2), M.MOE_ERR_INVALID_ARG),
+    (dict(quant=3), M.MOE_ERR_INVALID_ARG),
+    (dict(num_cus=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(max_tokens=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=4096, num_ranks=1), M.MOE_ERR_UNSUPPORTED),
+    (dict(max_tokens=1 << 28, num_topk=16), M.MOE_ERR_UNSUPPORTED),  # rows overflow int32
+])
+def test_config_validation(lib, kw, code):
+    assert M.moe_config_check(_cfg(**kw)) == code
+
+
+def test_null_config(lib):
+    assert lib.moe_config_check(None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_rows_capacity(None) == 0
+
+
+def _layout(lib, cfg, T, idx=FAKE, h=None, ws=FAKE, ws_bytes=1 << 20):
+    h = _handle() if h is None else h
+    return lib.moe_dispatch_layout(ctypes.byref(cfg), T, idx, ctypes.byref(h), ws, ws_bytes, None)
+
+
+def test_layout_argument_errors(lib):
+    c = _cfg()
+    assert _layout(lib, c, 65) == M.MOE_ERR_CAPACITY           # num_tokens > max_tokens
+    assert _layout(lib, c, -1) == M.MOE_ERR_INVALID_ARG
+    assert _layout(lib, c, 4, idx=None) == M.MOE_ERR_INVALID_ARG
+    assert _layout(lib, c, 4, idx=FAKE + 2) == M.MOE_ERR_INVALID_ARG   # misaligned
+    assert _layout(lib, c, 4, ws=None) == M.MOE_ERR_INVALID_ARG
+    assert _layout(lib, c, 4, ws_bytes=16) == M.MOE_ERR_CAPACITY
+    for f, _ in M.MoeHandle._fields_:
+        assert _layout(lib, c, 4, h=_handle(**{f: None})) == M.MOE_ERR_INVALID_ARG, f
+        assert _layout(lib, c, 4, h=_handle(**{f: FAKE + 1})) == M.MOE_ERR_INVALID_ARG, f
+    assert lib.moe_dispatch_layout(ctypes.byref(c), 4, FAKE, None, FAKE, 1 << 20, None) \
+        == M.MOE_ERR_INVALID_ARG
+    assert _layout(lib, _cfg(num_topk=40), 4) == M.MOE_ERR_INVALID_ARG
+
+
+def _dispatch(lib, cfg, T, x=FAKE, w=None, out=FAKE, scale=None, rw=None, h=None):
+    h = _handle() if h is None else h
+    return lib.moe_dispatch(ctypes.byref(cfg), T, x, w, ctypes.byref(h), out, scale, rw, None)
+
+
+def test_dispatch_argument_errors(lib):
+    c = _cfg()
+    f8 = _cfg(quant=M.QUANT_FP8_F32)
+    assert _dispatch(lib, c, 65) == M.MOE_ERR_CAPACITY
+    assert _dispatch(lib, c, -3) == M.MOE_ERR_INVALID_ARG
+    assert _dispatch(lib, c, 4, x=None) == M.MOE_ERR_INVALID_ARG
+    assert _dispatch(lib, c, 4, x=FAKE + 8) == M.MOE_ERR_INVALID_ARG      # needs 16-byte alignment
+    assert _dispatch(lib, c, 4, out=None) == M.MOE_ERR_INVALID_ARG
+    assert _dispatch(lib, c, 4, out=FAKE + 4) == M.MOE_ERR_INVALID_ARG
+    assert _dispatch(lib, c, 4, scale=FAKE) == M.MOE_ERR_INVALID_ARG      # no scales without FP8
+    assert _dispatch(lib, f8, 4) == M.MOE_ERR_INVALID_ARG                 # FP8 needs scales
+    assert _dispatch(lib, c, 4, rw=FAKE) == M.MOE_ERR_INVALID_ARG         # row weights need topk_w
+    assert _dispatch(lib, c, 4, h=_handle(pair_to_row=None)) == M.MOE_ERR_INVALID_ARG
+    # zero tokens: valid, nothing enqueued
+    assert _dispatch(lib, c, 0, x=None) == M.MOE_OK
+    assert _dispatch(lib, f8, 0, x=None, scale=FAKE) == M.MOE_OK
+
+
+def _combine(lib, cfg, T, y=FAKE, w=FAKE, out=FAKE, h=None):
+    h = _handle() if h is None else h
+    return lib.moe_combine(ctypes.byref(cfg), T, y, w, ctypes.byref(h), out, None)
+
+
+def test_combine_argument_errors(lib):
+    c = _cfg()
+    assert _combine(lib, c, 65) == M.MOE_ERR_CAPACITY
+    assert _combine(lib, c, -1) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, c, 3, y=None) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, c, 3, w=None) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, c, 3, out=None) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, c, 3, out=FAKE + 2) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, _cfg(hidden=12), 3) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, c, 3, h=_handle(status=None)) == M.MOE_ERR_INVALID_ARG
+    assert _combine(lib, c, 0, y=None, w=None, out=None) == M.MOE_OK
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    c = _cfg()
+    with pytest.raises(ValueError):
+        M._ptr(torch.zeros(4), 4, 0, "t")

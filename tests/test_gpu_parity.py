@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact for every integer and byte output (counts, offsets, both maps,
+status, every dispatched bf16 / E4M3 byte, every scale, every row weight) and
+for the bytes that must stay untouched: all output buffers start filled with a
+0xA5 sentinel on both sides and are compared whole, and 256-byte guard bands
+around each device buffer must survive.  Combine is checked against the
+tolerance |g - o| <= 1e-2 |o| + 1e-5 S, S = sum_k |w_k y_k| per element (the
+fp32 accumulation order is identical on both sides, so the expected result is
+exact equality; the count of unequal elements is reported).
+
+Every test prints the case it runs before touching the GPU.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_idx_amd as M
+import oracle
+from combine_topk_idx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0xA5
+GUARD = 256  # bytes
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    M.library()  # raises if libmoe_dispatch.so is not built
+    oracle._load()
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+class Guarded:
+    """A device buffer of `nbytes` inside 0xA5-filled guard bands."""
+
+    def __init__(self, nbytes, dtype, shape):
+        nbytes = int(nbytes)
+        self.nbytes = nbytes
+        self.full = torch.full((nbytes + 2 * GUARD,), SENT, dtype=torch.uint8, device="cuda")
+        self.view = self.full[GUARD:GUARD + nbytes].view(dtype).view(shape)
+
+    def host(self):
+        b = self.full.cpu().numpy()
+        assert np.all(b[:GUARD] == SENT) and np.all(b[GUARD + self.nbytes:] == SENT), \
+            "write outside the buffer (guard band changed)"
+        return b[GUARD:GUARD + self.nbytes]
+
+
+def _sentinel(nbytes):
+    return np.full(int(nbytes), SENT, np.uint8)
+
+
+def make_cfg(wl, T_max=None, num_cus=0):
+    return M.MoeConfig(max_tokens=wl.T if T_max is None else T_max, hidden=wl.H,
+                       num_experts=wl.E, num_topk=wl.K, num_ranks=wl.R, layout=wl.layout,
+                       align=wl.align, capacity=wl.capacity, quant=wl.quant, num_cus=num_cus)
+
+
+def scale_cols(wl):
+    nb = wl.H // 128
+    return {W.QUANT_NONE: 0, W.QUANT_FP8_F32: nb, W.QUANT_FP8_UE8M0: (nb + 3) // 4}[wl.quant]
+
+
+def run_gpu(wl, idx, w, x, y, cfg):
+    """One layout + dispatch + combine through the ABI; returns host arrays."""
+    T, K, E, R, H = idx.shape[0], wl.K, wl.E, wl.R, wl.H
+    rows = M.moe_rows_capacity(cfg)
+    handle = M.Handle.__new__(M.Handle)
+    bufs = {}
+    for name, n in (("expert_count", E), ("recv_count", E), ("expert_offset", E + 1),
+                    ("rank_offset", R + 1), ("pair_to_row", cfg.max_tokens * K),
+                    ("row_to_pair", rows), ("status", 2)):
+        g = Guarded(4 * n, torch.int32, (n,))
+        bufs[name] = g
+        setattr(handle, name, g.view)
+    handle.c = M.MoeHandle(*(bufs[n].view.data_ptr() for n, _ in M.MoeHandle._fields_))
+    ws = torch.empty(M.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    fp8 = wl.quant != W.QUANT_NONE
+    ebytes = 1 if fp8 else 2
+    out_x = Guarded(rows * H * ebytes, torch.uint8 if fp8 else torch.int16, (rows, H))
+    nsc = scale_cols(wl)
+    out_scale = Guarded(rows * nsc * 4, torch.int32, (rows, nsc)) if fp8 else None
+    out_rw = Guarded(rows * 4, torch.float32, (rows,))
+    out = Guarded(T * H * 2, torch.int16, (T, H))
+    d_idx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+    d_w = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    d_x = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    d_y = torch.from_numpy(np.ascontiguousarray(y).view(np.int16)).cuda()
+    M.moe_dispatch_layout(cfg, T, d_idx, handle, ws)
+    M.moe_dispatch(cfg, T, d_x, d_w, handle, out_x.view,
+                   out_scale.view if fp8 else None, out_rw.view)
+    M.moe_combine(cfg, T, d_y, d_w, handle, out.view)
+    torch.cuda.synchronize()
+    res = {n: g.host().view(np.int32) for n, g in bufs.items()}
+    res["out_x"] = out_x.host()
+    res["out_scale"] = out_scale.host() if fp8 else None
+    res["out_row_weight"] = out_rw.host()
+    res["out"] = out.host().view(np.uint16).reshape(T, H)
+    return res
+
+
+def run_oracle(wl, idx, w, x, y, cfg):
+    T, K, E, R, H = idx.shape[0], wl.K, wl.E, wl.R, wl.H
+    rows = M.moe_rows_capacity(cfg)
+    h = oracle.dispatch_layout(idx, E, R, wl.layout, wl.align, wl.capacity, rows_cap=rows)
+    res = {}
+    for name, n in (("expert_count", E), ("recv_count", E), ("expert_offset", E + 1),
+                    ("rank_offset", R + 1), ("pair_to_row", cfg.max_tokens * K),
+                    ("row_to_pair", rows), ("status", 2)):
+        a = _sentinel(4 * n).view(np.int32)
+        a[:h[name].size] = h[name]
+        res[name] = a
+    fp8 = wl.quant != W.QUANT_NONE
+    ox = _sentinel(rows * H * (1 if fp8 else 2))
+    nsc = scale_cols(wl)
+    osc = _sentinel(rows * nsc * 4) if fp8 else None
+    orw = _sentinel(rows * 4)
+    out_x = ox.view(np.uint8 if fp8 else np.uint16).reshape(rows, H)
+    out_scale = None
+    if wl.quant == W.QUANT_FP8_F32:
+        out_scale = osc.view(np.float32).reshape(rows, nsc)
+    elif wl.quant == W.QUANT_FP8_UE8M0:
+        out_scale = osc.view(np.uint32).reshape(rows, nsc)
+    oracle.dispatch(x, h["pair_to_row"], K, wl.quant, rows, topk_w=w, out_x=out_x,
+                    out_scale=out_scale, out_row_weight=orw.view(np.float32))
+    res["out_x"] = ox
+    res["out_scale"] = osc
+    res["out_row_weight"] = orw
+    res["out"] = oracle.combine(y, w, h["pair_to_row"]) if T > 0 else np.zeros((0, H), np.uint16)
+    return res
+
+
+def assert_combine_close(g, o, y, w, p2r, K):
+    """Q20 tolerance, evaluated where the bf16 results differ."""
+    diff = np.nonzero(g.reshape(-1) != o.reshape(-1))[0]
+    if diff.size == 0:
+        return 0
+    T, H = o.shape
+    t, j = diff // H, diff % H
+    gf = W.bf16_bits_to_f32(g.reshape(-1)[diff]).astype(np.float64)
+    of = W.bf16_bits_to_f32(o.reshape(-1)[diff]).astype(np.float64)
+    S = np.zeros(diff.size)
+    for k in range(K):
+        r = p2r.reshape(T, K)[t, k]
+        ok = r >= 0
+        yv = W.bf16_bits_to_f32(y[r[ok], j[ok]]).astype(np.float64)
+        S[ok] += np.abs(w[t[ok], k].astype(np.float64) * yv)
+    bad = np.abs(gf - of) > 1e-2 * np.abs(of) + 1e-5 * S
+    assert not bad.any(), f"{int(bad.sum())} combine elements outside tolerance"
+    return int(diff.size)
+
+
+def check_parity(wl, idx, w, x, y, cfg, label):
+    g = run_gpu(wl, idx, w, x, y, cfg)
+    o = run_oracle(wl, idx, w, x, y, cfg)
+    for name in ("expert_count", "recv_count", "expert_offset", "rank_offset", "status",
+                 "pair_to_row", "row_to_pair"):
+        if not np.array_equal(g[name], o[name]):
+            bad = np.nonzero(g[name] != o[name])[0]
+            raise AssertionError(f"{label}: {name} differs at {bad[:8]}: gpu {g[name][bad[:8]]} "
+                                 f"oracle {o[name][bad[:8]]}")
+    for name in ("out_x", "out_scale", "out_row_weight"):
+        if g[name] is None:
+            continue
+        if not np.array_equal(g[name], o[name]):
+            bad = np.nonzero(g[name] != o[name])[0]
+            raise AssertionError(f"{label}: {name} differs at {bad.size} bytes, first {bad[:8]}: "
+                                 f"gpu {g[name][bad[:8]]} oracle {o[name][bad[:8]]}")
+    n_ne = assert_combine_close(g["out"], o["out"], y, w, o["pair_to_row"], wl.K)
+    print(f"[ok] {label}: layout/dispatch bit-exact, combine unequal elements {n_ne}", flush=True)
+    return g, o
+
+
+def inputs_for(wl, row_to_pair=None):
+    inp = W.make_inputs(wl)
+    if wl.expert_output == "scaled":
+        h = oracle.dispatch_layout(inp.topk_idx, wl.E, wl.R, wl.layout, wl.align, wl.capacity)
+        y = W.expert_outputs(wl, inp, h["row_to_pair"])
+    else:
+        y = W.expert_outputs(wl, inp)
+    return inp.topk_idx, inp.topk_w, inp.x, y
+
+
+# ---- every workload at its full size, in the launch configuration the benchmark times
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_size(name):
+    wl = W.WORKLOADS[name]
+    _say(f"full-size workload {name}")
+    idx, w, x, y = inputs_for(wl)
+    cfg = make_cfg(wl)
+    g, o = check_parity(wl, idx, w, x, y, cfg, name)
+    if wl.layout == W.LAYOUT_MASKED:
+        print(f"[info] {name}: dropped pairs {int(g['status'][0])}", flush=True)
+    # determinism: a second run is bitwise identical
+    g2 = run_gpu(wl, idx, w, x, y, cfg)
+    for k in g:
+        if g[k] is not None:
+            assert np.array_equal(g[k], g2[k]), f"{name}: {k} not deterministic"
+
+
+# ---- small cases spanning several tiles and ragged tails
+
+SMALL = [
+    # T, H, E, K, R, layout, align, capacity, quant
+    (37, 384, 24, 6, 4, W.LAYOUT_CONTIGUOUS, 16, 1, W.QUANT_FP8_UE8M0),
+    (37, 384, 24, 6, 4, W.LAYOUT_CONTIGUOUS, 16, 1, W.QUANT_FP8_F32),
+    (300, 640, 40, 7, 8, W.LAYOUT_CONTIGUOUS, 3, 1, W.QUANT_FP8_UE8M0),   # 5 blocks: partial word
+    (300, 1152, 40, 7, 5, W.LAYOUT_MASKED, 1, 33, W.QUANT_FP8_F32),       # overflow
+    (513, 72, 17, 3, 17, W.LAYOUT_CONTIGUOUS, 5, 1, W.QUANT_NONE),        # H % 512 ragged
+    (513, 1032, 64, 5, 2, W.LAYOUT_MASKED, 1, 20, W.QUANT_NONE),
+    (2000, 256, 96, 32, 8, W.LAYOUT_CONTIGUOUS, 8, 1, W.QUANT_FP8_F32),   # K = 32
+    (4100, 128, 8, 1, 1, W.LAYOUT_MASKED, 1, 700, W.QUANT_FP8_UE8M0),     # K = 1, H = 128
+    (9000, 512, 256, 8, 8, W.LAYOUT_CONTIGUOUS, 128, 1, W.QUANT_FP8_UE8M0),  # > 64 layout chunks
+    (1, 2048, 128, 8, 8, W.LAYOUT_MASKED, 1, 128, W.QUANT_FP8_F32),       # T = 1
+    (64, 8, 4, 4, 4, W.LAYOUT_CONTIGUOUS, 1, 1, W.QUANT_NONE),            # H = 8, E = R
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_K{c[3]}_L{c[5]}_Q{c[8]}"
+                                             for c in SMALL])
+def test_small_ragged(case):
+    T, H, E, K, R, layout, align, cap, quant = case
+    _say(f"small {case}")
+    wl = W.Workload("small", T=T, H=H, E=E, K=K, R=R, layout=layout, align=align,
+                    capacity=cap, quant=quant, routing="softmax", seed=1000 + T)
+    idx, w, x, y = inputs_for(wl)
+    check_parity(wl, idx, w, x, y, make_cfg(wl), f"small {case}")
+
+
+def _edge_inputs(kind, T, H, E, K, rng):
+    if kind == "one_expert":
+        idx = np.zeros((T, K), np.int32)
+        idx[:, 1:] = -1
+    elif kind == "invalid_and_unrouted":
+        idx = rng.integers(0, E, (T, K)).astype(np.int32)
+        m = rng.random((T, K))
+        idx[m < 0.2] = -1
+        idx[(m >= 0.2) & (m < 0.3)] = E + 5
+        idx[(m >= 0.3) & (m < 0.35)] = -7
+        idx[7] = -1
+    elif kind == "duplicates":
+        idx = rng.integers(0, 3, (T, K)).astype(np.int32)
+    else:
+        raise ValueError(kind)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    xf = rng.standard_normal((T, H)).astype(np.float32)
+    xf[0] *= 1e-39          # bf16 subnormals
+    xf[1, :128] = 0.0       # zero block
+    xf[2, :128] = -0.0      # negative zero block
+    xf[3] *= 3e-11          # block maxima around the amax floor
+    xf[4] *= 1e30
+    return idx, w, W.f32_to_bf16_bits(xf)
+
+
+@pytest.mark.parametrize("kind", ["one_expert", "invalid_and_unrouted", "duplicates"])
+@pytest.mark.parametrize("layout,quant", [(W.LAYOUT_CONTIGUOUS, W.QUANT_FP8_UE8M0),
+                                          (W.LAYOUT_MASKED, W.QUANT_FP8_F32),
+                                          (W.LAYOUT_MASKED, W.QUANT_NONE)])
+def test_edge_routing(kind, layout, quant):
+    T, H, E, K, R = 200, 256, 12, 4, 3
+    _say(f"edge {kind} layout {layout} quant {quant}")
+    rng = np.random.default_rng(zlib.crc32(f"{kind}/{layout}/{quant}".encode()))
+    wl = W.Workload("edge", T=T, H=H, E=E, K=K, R=R, layout=layout, align=4, capacity=9,
+                    quant=quant)
+    idx, w, x = _edge_inputs(kind, T, H, E, K, rng)
+    y = W.f32_to_bf16_bits(rng.standard_normal((wl.rows_capacity, H)).astype(np.float32))
+    g, o = check_parity(wl, idx, w, x, y, make_cfg(wl), f"edge {kind}")
+    if kind == "invalid_and_unrouted":
+        assert g["status"][1] > 0
+
+
+def test_capacity_one_masked():
+    T, H, E, K, R = 100, 128, 8, 2, 8
+    _say("masked capacity 1")
+    wl = W.Workload("cap1", T=T, H=H, E=E, K=K, R=R, layout=W.LAYOUT_MASKED, capacity=1,
+                    quant=W.QUANT_FP8_UE8M0, seed=7)
+    idx, w, x, y = inputs_for(wl)
+    g, _ = check_parity(wl, idx, w, x, y, make_cfg(wl), "masked capacity 1")
+    assert g["status"][0] == T * K - E
+
+
+def test_fewer_tokens_than_max_and_num_cus():
+    """A call with num_tokens < max_tokens, and a restricted compute-unit budget."""
+    wl = W.WORKLOADS["deepseekv3_decode_T256"].replace(T=200)
+    _say("T=200 of max 256, num_cus=7")
+    idx, w, x, y = inputs_for(wl.replace(T=200))
+    cfg = make_cfg(wl, T_max=256, num_cus=7)
+    check_parity(wl, idx, w, x, y, cfg, "T<max, num_cus=7")
+
+
+def test_zero_tokens_layout():
+    wl = W.Workload("empty", T=0, H=256, E=16, K=4, R=4, layout=W.LAYOUT_CONTIGUOUS, align=8)
+    _say("zero tokens")
+    cfg = make_cfg(wl, T_max=50)
+    idx = np.zeros((0, 4), np.int32)
+    w = np.zeros((0, 4), np.float32)
+    x = np.zeros((0, 256), np.uint16)
+    y = np.zeros((M.moe_rows_capacity(cfg), 256), np.uint16)
+    g, _ = check_parity(wl, idx, w, x, y, cfg, "zero tokens")
+    assert np.all(g["row_to_pair"] == -1) and not g["expert_offset"].any()
+
+
+def test_quant_sweep_all_bf16_magnitudes():
+    """Every bf16 value with |x| <= 448 goes through the E4M3 conversion with
+    scale exactly 1 (UE8M0 k = 0 and fp32 s = 1): block element 0 is 448, the
+    other 127 carry the sweep.  Blocks whose maximum is 448 * 2^j sweep the
+    same values scaled by powers of two (exact ties included)."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = W.bf16_bits_to_f32(b)
+    vals = f[np.isfinite(f) & (np.abs(f) <= 448)]
+    per = 127
+    nblk = -(-vals.size // per)
+    pad = np.zeros(nblk * per, np.float32)
+    pad[:vals.size] = vals
+    blocks = np.concatenate([np.full((nblk, 1), 448.0, np.float32), pad.reshape(nblk, per)], 1)
+    scaled = [blocks * np.float32(2.0 ** j) for j in (0, -3, 5)]
+    allb = np.concatenate(scaled).reshape(-1)
+    H = 7168
+    T = -(-allb.size // H)
+    xf = np.zeros(T * H, np.float32)
+    xf[:allb.size] = allb
+    x = W.f32_to_bf16_bits(xf.reshape(T, H))
+    rng = np.random.default_rng(77)
+    for quant in (W.QUANT_FP8_UE8M0, W.QUANT_FP8_F32):
+        _say(f"bf16 magnitude sweep quant {quant} T={T}")
+        wl = W.Workload("sweep", T=T, H=H, E=4, K=2, R=2, layout=W.LAYOUT_CONTIGUOUS,
+                        align=1, quant=quant)
+        idx = np.stack([np.arange(T) % 4, (np.arange(T) + 1) % 4], 1).astype(np.int32)
+        w = np.full((T, 2), 0.5, np.float32)
+        y = W.f32_to_bf16_bits(rng.standard_normal((wl.rows_capacity, H)).astype(np.float32))
+        check_parity(wl, idx, w, x, y, make_cfg(wl), f"sweep quant {quant}")
