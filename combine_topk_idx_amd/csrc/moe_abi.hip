@@ -104,7 +104,8 @@ int device_cu_count()
 // flight.  Short batches (decode) split rows further so the launch still has
 // several waves per compute unit; num_cus > 0 caps the grid and the waves
 // stride over the items.
-RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters, int32_t num_cus)
+RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters, int32_t num_cus,
+                 int32_t min_items_per_token)
 {
     RowPlan p;
     p.width = width;
@@ -112,6 +113,8 @@ RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters, int32_t
     const int cus = device_cu_count();
     const int64_t target_waves = (int64_t)cus * 8;
     int64_t per_token = (p.n_iters + max_iters - 1) / max_iters;
+    if (per_token < min_items_per_token)
+        per_token = min_items_per_token < p.n_iters ? min_items_per_token : p.n_iters;
     if ((int64_t)T * per_token < target_waves && T > 0) {
         const int64_t want = (target_waves + T - 1) / T;
         per_token = want < p.n_iters ? want : p.n_iters;
@@ -148,9 +151,8 @@ size_t moe_workspace_bytes(const moe_config_t *cfg)
 {
     if (check_config(cfg) != MOE_OK)
         return 0;
-    const LayoutPlan lp = layout_plan((int64_t)cfg->max_tokens * cfg->num_topk);
-    const size_t bytes = sizeof(int32_t) * (size_t)lp.nblocks * (size_t)(cfg->num_experts + 1);
-    return (bytes + 255) / 256 * 256;
+    const size_t slots = sizeof(int32_t) * (size_t)cfg->max_tokens * (size_t)cfg->num_topk;
+    return layout_table_bytes(cfg->num_experts) + (slots + 255) / 256 * 256;
 }
 
 moe_status_t moe_config_check(const moe_config_t *cfg) { return check_config(cfg); }
@@ -167,11 +169,12 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens, co
     if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
         return st;
     if ((num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4))) || workspace == nullptr ||
-        !aligned(workspace, 4))
+        !aligned(workspace, 16))
         return MOE_ERR_INVALID_ARG;
     const int64_t P = (int64_t)num_tokens * cfg->num_topk;
-    const LayoutPlan lp = layout_plan(P);
-    if (workspace_bytes < sizeof(int32_t) * (size_t)lp.nblocks * (size_t)(cfg->num_experts + 1))
+    const LayoutPlan lp = layout_plan(P, cfg->num_experts);
+    const size_t table = layout_table_bytes(cfg->num_experts);
+    if (workspace_bytes < table + sizeof(int32_t) * (size_t)P)
         return MOE_ERR_CAPACITY;
 
     LayoutArgs a;
@@ -185,11 +188,13 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens, co
     a.capacity = cfg->layout == MOE_LAYOUT_MASKED ? cfg->capacity : 1;
     a.rows_cap = (int32_t)rows_capacity64(*cfg);
     a.nbits = bits_for(cfg->num_experts);
+    a.rounds = lp.rounds;
     a.chunk = lp.chunk;
     a.nblocks = lp.nblocks;
     a.ws = static_cast<int32_t *>(workspace);
+    a.slots = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + table);
     a.h = *handle;
-    return from_hip(launch_layout(a, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_layout(a, lp, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x, const float *topk_w,
@@ -256,7 +261,8 @@ moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint
     a.T = num_tokens;
     a.K = cfg->num_topk;
     a.H = cfg->hidden;
-    a.plan = row_plan(num_tokens, cfg->hidden, kCombineWidth, kCombineMaxIters, cfg->num_cus);
+    a.plan = row_plan(num_tokens, cfg->hidden, kCombineWidth, kCombineMaxIters, cfg->num_cus,
+                      kCombineMinItemsPerToken);
     return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 

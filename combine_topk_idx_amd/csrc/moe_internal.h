@@ -15,8 +15,8 @@ constexpr int kWavesPerBlock = kBlockThreads / kWave;
 constexpr int kQuantGroup = 128;      // 1x128 activation quantization group
 constexpr int kMaxTopk = 32;
 constexpr int kMaxExperts = 2048;     // layout keeps 7 int32 per expert in LDS
-constexpr int kLayoutMaxBlocks = 64;  // cap on layout workgroups (bounds the workspace)
-constexpr int kLayoutChunkUnit = 1024;
+constexpr int kLayoutMaxBlocks = 64;  // cap on layout blocks (columns of the histogram table)
+constexpr int64_t kSingleMaxPairs = 65536;  // largest batch the one-launch layout takes
 
 // ---- layout ---------------------------------------------------------------
 
@@ -27,17 +27,21 @@ struct LayoutArgs {
     int32_t layout, align, capacity;
     int32_t rows_cap;   // rows of row_to_pair
     int32_t nbits;      // bits needed to tell experts apart (ballot match)
-    int32_t chunk;      // pairs per workgroup, multiple of 4 * 64
-    int32_t nblocks;    // workgroups = ceil(P / chunk), >= 1
-    int32_t *ws;        // [nblocks][E + 1] block histograms (+ invalid count)
+    int32_t rounds;     // runs of 64 pairs per wave
+    int32_t chunk;      // pairs per block = waves * 64 * rounds
+    int32_t nblocks;    // blocks = ceil(P / chunk), >= 1, <= kLayoutMaxBlocks
+    int32_t *ws;        // [E + 1][kLayoutMaxBlocks] per-block histograms (row E: invalid ids)
+    int32_t *slots;     // [P] slot of each pair among its expert's pairs inside its block
     moe_handle_t h;
 };
 
 struct LayoutPlan {
-    int32_t chunk, nblocks;
+    int32_t waves, rounds, chunk, nblocks;
+    bool single;  // one launch, every block histograms all pairs (small batches)
 };
-LayoutPlan layout_plan(int64_t P);
-hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+LayoutPlan layout_plan(int64_t P, int32_t E);
+size_t layout_table_bytes(int32_t E);
+hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_t stream);
 
 // ---- dispatch / combine -----------------------------------------------------
 
@@ -74,7 +78,7 @@ struct CombineArgs {
 
 int device_cu_count();
 RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item,
-                 int32_t num_cus);
+                 int32_t num_cus, int32_t min_items_per_token = 1);
 hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
@@ -84,7 +88,8 @@ constexpr int kDispatchBf16Width = kWave * 8;    // 8 bf16 = 16 bytes per lane
 constexpr int kDispatchBf16MaxIters = 16;
 constexpr int kDispatchFp8Width = kWave * 16;    // 16 channels per lane, 8 lanes per block
 constexpr int kDispatchFp8MaxIters = 8;
-constexpr int kCombineWidth = kWave * 8;         // 8 bf16 per lane
+constexpr int kCombineWidth = kWave * 16;        // two vectors of 8 bf16 per lane
 constexpr int kCombineMaxIters = 64;
+constexpr int kCombineMinItemsPerToken = 2;      // rows split in two: more, shorter waves
 
 }  // namespace moe

@@ -8,20 +8,34 @@
 // layouts paragraph).  Rows of one expert keep ascending pair order, i.e. the
 // result is a stable counting sort of the pairs by expert.
 //
-// Two launches, no atomics that decide an order:
-//   layout_count  one workgroup per chunk of pairs: LDS histogram of its chunk
-//                 -> workspace row [block][E], plus its invalid-id count.
-//   layout_index  one workgroup per chunk again: every workgroup reads the
-//                 whole (small) histogram table, derives the segment offsets
-//                 and its own cross-chunk prefix, then ranks its pairs with
-//                 64-lane ballot matching (stable inside a wave), writes both
-//                 maps, the padding rows of its share of experts, and block 0
-//                 writes the counts, offsets and status.
+// Pairs are cut into blocks of `chunk` consecutive pairs; wave w of a block
+// owns `rounds` runs of 64 pairs.  A 64-lane ballot match gives each pair its
+// rank among equal experts in its run, an LDS scan over the block's waves
+// turns that into its slot inside the block, and
+//     row = segment_offset[e] + (pairs of e in earlier blocks) + slot.
+// No atomic decides an order, so the result is deterministic.  Two schedules
+// produce the same result:
+//   layout_single  (up to kSingleMaxPairs pairs, E <= 512) one launch, no
+//                  workspace: every block histograms ALL pairs itself (64-bit
+//                  LDS atomics: all pairs in the low word, pairs before the
+//                  block in the high word), so it needs nothing from other
+//                  blocks.  The redundant histogram costs about as much as a
+//                  second launch would, and no table round trip is needed.
+//   layout_rank + layout_index  (larger batches) the rank kernel writes each
+//                  pair's slot and its block histogram (one column of an
+//                  expert-major table in the workspace); the index kernel
+//                  reads the table cooperatively (one 16-byte vector per
+//                  thread) and writes the rows.
+// Both end with the same steps: segment offsets by a block-wide scan, the
+// pair <-> row maps, padding rows filled with -1 (one expert per wave over
+// the grid), and block 0 publishing counts, offsets and status.
 #include "moe_internal.h"
 
 namespace moe {
 
 namespace {
+
+constexpr int kTileRounds = 16;  // runs of 64 pairs a lane keeps in registers
 
 // Lanes of the wave holding the same routed expert as this lane: one ballot
 // per expert-id bit.  Returns 0 for lanes that are not routed.
@@ -39,79 +53,160 @@ __device__ __forceinline__ uint64_t match_expert(int32_t e, bool routed, int nbi
 // Number of set bits of m below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m)
 {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__global__ __launch_bounds__(kBlockThreads) void layout_count(LayoutArgs a)
-{
-    extern __shared__ int32_t hist[];  // [E + 1], hist[E] = invalid ids
-    const int tid = threadIdx.x;
-    for (int i = tid; i <= a.E; i += kBlockThreads)
-        hist[i] = 0;
-    __syncthreads();
+// Pair range [w0, w1) of wave `wave` in block `blk`.
+struct WaveRange {
+    int64_t w0, w1;
+};
 
-    const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+__device__ __forceinline__ WaveRange wave_range(const LayoutArgs &a, int blk, int wave)
+{
+    const int64_t c0 = (int64_t)blk * a.chunk;
     const int64_t c1 = min(a.P, c0 + a.chunk);
-    int invalid = 0;
-    for (int64_t p = c0 + tid; p < c1; p += kBlockThreads) {
-        const int32_t e = a.topk_idx[p];
-        if (e >= 0 && e < a.E)
-            atomicAdd(&hist[e], 1);
-        else if (e != -1)
-            ++invalid;
-    }
-    if (invalid)
-        atomicAdd(&hist[a.E], invalid);
-    __syncthreads();
-
-    int32_t *row = a.ws + (int64_t)blockIdx.x * (a.E + 1);
-    for (int i = tid; i <= a.E; i += kBlockThreads)
-        row[i] = hist[i];
+    WaveRange r;
+    r.w0 = min(c1, c0 + (int64_t)wave * kWave * a.rounds);
+    r.w1 = min(c1, r.w0 + (int64_t)kWave * a.rounds);
+    return r;
 }
 
-__global__ __launch_bounds__(kBlockThreads) void layout_index(LayoutArgs a)
+// Load runs [base, base + 64*kTileRounds) of a non-empty range ending at w1
+// from src; lanes past the end get `fill`.  Runs that start past the end are
+// skipped by a wave-uniform test; inside a run the address is clamped into
+// the range so the load needs no lane mask.
+__device__ __forceinline__ void load_runs(int32_t (&v)[kTileRounds], const int32_t *src, int64_t base,
+                                          int64_t w1, int lane, int32_t fill)
 {
-    extern __shared__ int32_t lds[];
-    const int E = a.E;
-    int32_t *tot = lds;              // [E]   pairs per expert, all chunks
-    int32_t *pre = tot + E;          // [E]   pairs per expert in earlier chunks
-    int32_t *off = pre + E;          // [E+1] segment starts
-    int32_t *cnt = off + E + 1;      // [4][E] per-wave counts, then per-wave slot bases
-    __shared__ int32_t red[kWavesPerBlock * 2];
+    int32_t raw[kTileRounds];
+#pragma unroll
+    for (int r = 0; r < kTileRounds; ++r) {
+        const int64_t p = base + (int64_t)r * kWave + lane;
+        raw[r] = fill;
+        if (base + (int64_t)r * kWave < w1)
+            raw[r] = src[p < w1 ? p : w1 - 1];
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRounds; ++r)
+        v[r] = base + (int64_t)r * kWave + lane < w1 ? raw[r] : fill;
+}
 
+__global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
+{
+    extern __shared__ int32_t cnt[];  // [WB][E]: per-wave counts, then per-wave slot bases
+    __shared__ int32_t red[1024 / kWave];
+    const int E = a.E;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    const int nwaves = blockDim.x / kWave;
     const int blk = blockIdx.x;
-    const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
+    const WaveRange wr = wave_range(a, blk, wave);
+    const bool one_tile = wr.w1 - wr.w0 <= (int64_t)kTileRounds * kWave;
 
-    // 1. totals and this chunk's prefix, from the histogram table (no pairs:
-    //    the count kernel did not run and the table is not read)
-    const int table_rows = a.P > 0 ? a.nblocks : 0;
-    for (int e = tid; e < E; e += kBlockThreads) {
-        int32_t t = 0, p = 0;
-        for (int b = 0; b < table_rows; ++b) {
-            const int32_t v = a.ws[(int64_t)b * (E + 1) + e];
-            t += v;
-            p += b < blk ? v : 0;
-        }
-        tot[e] = t;
-        pre[e] = p;
-    }
-    for (int i = tid; i < kWavesPerBlock * E; i += kBlockThreads)
+    int32_t id[kTileRounds];
+    if (wr.w0 < wr.w1)
+        load_runs(id, a.topk_idx, wr.w0, wr.w1, lane, -1);
+    for (int i = tid; i < nwaves * E; i += blockDim.x)
         cnt[i] = 0;
     __syncthreads();
 
-    // 2. segment offsets: exclusive scan of padded sizes (contiguous) or e*C
-    if (contiguous) {
-        const int per = (E + kBlockThreads - 1) / kBlockThreads;
+    // 1. rank of each pair among equal experts earlier in its wave's runs
+    int32_t *mycnt = cnt + wave * E;
+    int32_t rank[kTileRounds];
+    int invalid = 0;
+    for (int64_t base = wr.w0; base < wr.w1; base += (int64_t)kTileRounds * kWave) {
+        if (base != wr.w0)
+            load_runs(id, a.topk_idx, base, wr.w1, lane, -1);
+#pragma unroll
+        for (int r = 0; r < kTileRounds; ++r) {
+            rank[r] = 0;
+            if (base + (int64_t)r * kWave >= wr.w1)
+                continue;  // wave-uniform
+            const int32_t e = id[r];
+            const bool in = base + (int64_t)r * kWave + lane < wr.w1;
+            const bool routed = e >= 0 && e < E;
+            invalid += (in && !routed && e != -1) ? 1 : 0;
+            const uint64_t m = match_expert(e, routed, a.nbits);
+            if (routed) {
+                const int below = lanes_below(m);
+                const int32_t first = mycnt[e];     // read by every lane of the match ...
+                rank[r] = first + below;
+                if (below == 0)
+                    mycnt[e] = first + __popcll(m);  // ... before its leader advances it
+            }
+        }
+    }
+    for (int d = kWave / 2; d > 0; d >>= 1)
+        invalid += __shfl_xor(invalid, d);
+    if (lane == 0)
+        red[wave] = invalid;
+    __syncthreads();
+
+    // 2. per-wave slot bases inside the block; block histogram -> table column
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t s = 0;
+        for (int w = 0; w < nwaves; ++w) {
+            const int32_t c = cnt[w * E + e];
+            cnt[w * E + e] = s;
+            s += c;
+        }
+        a.ws[(int64_t)e * kLayoutMaxBlocks + blk] = s;
+    }
+    if (tid == 0) {
+        int32_t v = 0;
+        for (int w = 0; w < nwaves; ++w)
+            v += red[w];
+        a.ws[(int64_t)E * kLayoutMaxBlocks + blk] = v;
+    }
+    __syncthreads();
+
+    // 3. slot of each pair inside the block
+    for (int64_t base = wr.w0; base < wr.w1; base += (int64_t)kTileRounds * kWave) {
+        if (!one_tile)
+            load_runs(id, a.topk_idx, base, wr.w1, lane, -1);
+#pragma unroll
+        for (int r = 0; r < kTileRounds; ++r) {
+            if (base + (int64_t)r * kWave >= wr.w1)
+                continue;  // wave-uniform
+            const int64_t p = base + (int64_t)r * kWave + lane;
+            const int32_t e = id[r];
+            const bool routed = e >= 0 && e < E;
+            int32_t slot = -1;
+            if (one_tile) {
+                if (routed)
+                    slot = mycnt[e] + rank[r];
+            } else {
+                // several tiles: ranks were not kept, match again from the bases
+                const uint64_t m = match_expert(e, routed, a.nbits);
+                if (routed) {
+                    const int below = lanes_below(m);
+                    const int32_t first = mycnt[e];
+                    slot = first + below;
+                    if (below == 0)
+                        mycnt[e] = first + __popcll(m);
+                }
+            }
+            if (p < wr.w1)
+                a.slots[p] = slot;
+        }
+    }
+}
+
+// ---- steps shared by both schedules -----------------------------------------
+
+// off[0..E] = segment starts: exclusive scan of align-padded totals
+// (contiguous) or e * capacity (masked).  Block-wide; ends with a barrier.
+__device__ void segment_offsets(const LayoutArgs &a, const int32_t *tot, int32_t *off, int32_t *red)
+{
+    const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    if (a.layout == MOE_LAYOUT_CONTIGUOUS) {
+        const int per = (E + blockDim.x - 1) / blockDim.x;
         const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
         int32_t local = 0;
         for (int e = e0; e < e1; ++e)
             local += (tot[e] + a.align - 1) / a.align * a.align;
-        // inclusive scan of `local` over the wave
-        int32_t incl = local;
+        int32_t incl = local;  // inclusive scan over the wave
         for (int d = 1; d < kWave; d <<= 1) {
             const int32_t v = __shfl_up(incl, d);
             if (lane >= d)
@@ -128,34 +223,240 @@ __global__ __launch_bounds__(kBlockThreads) void layout_index(LayoutArgs a)
             off[e] = run;
             run += (tot[e] + a.align - 1) / a.align * a.align;
         }
-        if (tid == kBlockThreads - 1)
+        if (tid == blockDim.x - 1)
             off[E] = run;
     } else {
-        for (int e = tid; e <= E; e += kBlockThreads)
+        for (int e = tid; e <= E; e += blockDim.x)
             off[e] = e * a.capacity;
     }
+    __syncthreads();
+}
 
-    // 3. each wave counts its quarter of the chunk
-    const int64_t c0 = (int64_t)blk * a.chunk;
-    const int64_t c1 = min(a.P, c0 + a.chunk);
-    const int quarter = a.chunk / kWavesPerBlock;
-    const int64_t q0 = min(c1, c0 + (int64_t)wave * quarter);
-    const int64_t q1 = min(c1, q0 + quarter);
-    int32_t *mycnt = cnt + wave * E;
-    for (int64_t base = q0; base < q1; base += kWave) {
-        const int64_t p = base + lane;
-        const int32_t e = p < q1 ? a.topk_idx[p] : -1;
-        const bool routed = p < q1 && e >= 0 && e < E;
-        const uint64_t m = match_expert(e, routed, a.nbits);
-        if (routed && lanes_below(m) == 0)
-            mycnt[e] += __popcll(m);
+// Row of a routed pair of expert e whose slot among e's pairs is s, or -1
+// when it is dropped by the masked capacity.
+__device__ __forceinline__ int32_t row_of(const LayoutArgs &a, const int32_t *off, int32_t e, int32_t s)
+{
+    if (a.layout == MOE_LAYOUT_CONTIGUOUS)
+        return off[e] + s;
+    return s < a.capacity ? e * a.capacity + s : -1;
+}
+
+// row_to_pair = -1 for rows that hold no pair: the padding after each
+// expert's rows (one expert per wave over the grid) and a slice of the tail
+// past the last segment per wave.
+__device__ void fill_unused_rows(const LayoutArgs &a, const int32_t *tot, const int32_t *off)
+{
+    const int lane = threadIdx.x & (kWave - 1), nwaves = blockDim.x / kWave;
+    const int gwave = blockIdx.x * nwaves + (int)(threadIdx.x / kWave);
+    const int gwaves = a.nblocks * nwaves;
+    const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
+    for (int e = gwave; e < a.E; e += gwaves) {
+        const int32_t used = contiguous ? tot[e] : min(tot[e], a.capacity);
+        for (int32_t r = off[e] + used + lane; r < off[e + 1]; r += kWave)
+            a.h.row_to_pair[r] = -1;
+    }
+    const int64_t tail0 = off[a.E];
+    const int64_t span = (a.rows_cap - tail0 + gwaves - 1) / gwaves;
+    const int64_t r0 = tail0 + (int64_t)gwave * span;
+    const int64_t r1 = min((int64_t)a.rows_cap, r0 + span);
+    for (int64_t r = r0 + lane; r < r1; r += kWave)
+        a.h.row_to_pair[r] = -1;
+}
+
+// Block 0 only: counts, offsets, rank offsets and status.  `invalid` is the
+// block's total of invalid ids (valid in thread 0).
+__device__ void publish(const LayoutArgs &a, const int32_t *tot, const int32_t *off, int32_t *red,
+                        int32_t invalid)
+{
+    const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
+    int32_t overflow = 0;
+    for (int e = tid; e < E; e += blockDim.x) {
+        a.h.expert_count[e] = tot[e];
+        a.h.recv_count[e] = contiguous ? tot[e] : min(tot[e], a.capacity);
+        a.h.expert_offset[e] = off[e];
+        if (!contiguous)
+            overflow += max(0, tot[e] - a.capacity);
+    }
+    for (int r = tid; r <= a.R; r += blockDim.x)
+        a.h.rank_offset[r] = off[r * a.L];
+    for (int d = kWave / 2; d > 0; d >>= 1)
+        overflow += __shfl_xor(overflow, d);
+    __syncthreads();  // `red` is reused
+    if (lane == 0)
+        red[wave] = overflow;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t o = 0;
+        for (int w = 0; w < nwaves; ++w)
+            o += red[w];
+        a.h.expert_offset[E] = off[E];
+        a.h.status[0] = o;
+        a.h.status[1] = invalid;
+    }
+}
+
+// ---- schedule 2: index kernel -------------------------------------------------
+
+__global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
+{
+    extern __shared__ int32_t lds[];
+    const int E = a.E;
+    int32_t *tot = lds;          // [E+1] pairs per expert, all blocks ([E]: invalid ids)
+    int32_t *pre = tot + E + 1;  // [E+1] pairs per expert in earlier blocks
+    int32_t *off = pre + E + 1;  // [E+1] segment starts
+    __shared__ int32_t red[1024 / kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int blk = blockIdx.x;
+    const WaveRange wr = wave_range(a, blk, wave);
+    const bool one_tile = wr.w1 - wr.w0 <= (int64_t)kTileRounds * kWave;
+
+    // in flight while the table is read: the wave's ids and slots
+    int32_t id[kTileRounds], slot[kTileRounds];
+    if (wr.w0 < wr.w1) {
+        load_runs(id, a.topk_idx, wr.w0, wr.w1, lane, -1);
+        load_runs(slot, a.slots, wr.w0, wr.w1, lane, -1);
+    }
+
+    // 1. totals and this block's prefix from the expert-major table (row E:
+    //    invalid ids).  Each thread reads one 16-byte vector (4 columns) and
+    //    adds its partial sums into LDS; columns >= nblocks are masked (no
+    //    pairs: the rank kernel did not run and every column is masked).
+    for (int e = tid; e <= E; e += blockDim.x) {
+        tot[e] = 0;
+        pre[e] = 0;
+    }
+    __syncthreads();
+    const int cols = a.P > 0 ? a.nblocks : 0;
+    const int nvec = (E + 1) * (kLayoutMaxBlocks / 4);
+    for (int vi = tid; vi < nvec; vi += blockDim.x) {
+        const int e = vi / (kLayoutMaxBlocks / 4), j = vi % (kLayoutMaxBlocks / 4);
+        const int4 v = reinterpret_cast<const int4 *>(a.ws)[vi];
+        const int32_t c[4] = {v.x, v.y, v.z, v.w};
+        int32_t s = 0, p = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = 4 * j + q;
+            const int32_t x = b < cols ? c[q] : 0;
+            s += x;
+            p += b < blk ? x : 0;
+        }
+        if (s)
+            atomicAdd(&tot[e], s);
+        if (p)
+            atomicAdd(&pre[e], p);
     }
     __syncthreads();
 
-    // 4. slot base of each wave for each expert
-    for (int e = tid; e < E; e += kBlockThreads) {
-        int32_t s = pre[e];
-        for (int w = 0; w < kWavesPerBlock; ++w) {
+    // 2. segment offsets
+    segment_offsets(a, tot, off, red);
+
+    // 3. rows and both maps
+    for (int64_t base = wr.w0; base < wr.w1; base += (int64_t)kTileRounds * kWave) {
+        if (!one_tile) {
+            load_runs(id, a.topk_idx, base, wr.w1, lane, -1);
+            load_runs(slot, a.slots, base, wr.w1, lane, -1);
+        }
+#pragma unroll
+        for (int r = 0; r < kTileRounds; ++r) {
+            const int64_t p = base + (int64_t)r * kWave + lane;
+            if (base + (int64_t)r * kWave >= wr.w1)
+                continue;  // wave-uniform
+            const int32_t e = id[r];
+            const int32_t row = e >= 0 && e < E ? row_of(a, off, e, pre[e] + slot[r]) : -1;
+            if (p < wr.w1) {
+                a.h.pair_to_row[p] = row;
+                if (row >= 0)
+                    a.h.row_to_pair[row] = (int32_t)p;
+            }
+        }
+    }
+
+    // 4. rows that hold no pair; 5. block 0 publishes
+    fill_unused_rows(a, tot, off);
+    if (blk == 0)
+        publish(a, tot, off, red, tot[E]);
+}
+
+// ---- schedule 1: one launch ---------------------------------------------------
+
+__global__ __launch_bounds__(1024) void layout_single(LayoutArgs a)
+{
+    extern __shared__ int32_t lds[];
+    const int E = a.E;
+    unsigned long long *hist = reinterpret_cast<unsigned long long *>(lds);  // [E] low: all, high: earlier blocks
+    int32_t *tot = lds + 2 * E;  // [E]
+    int32_t *off = tot + E;      // [E+1]
+    int32_t *cnt = off + E + 1;  // [WB][E] per-wave counts, then per-wave slot bases
+    __shared__ int32_t red[1024 / kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const int blk = blockIdx.x;
+    const int64_t c0 = (int64_t)blk * a.chunk;  // one run of 64 pairs per wave
+
+    // own pair, in flight while LDS is cleared
+    const int64_t p = c0 + (int64_t)wave * kWave + lane;
+    const bool own = p < a.P && p < c0 + a.chunk;
+    const int32_t e_own = own ? a.topk_idx[p] : -1;
+    for (int i = tid; i < E; i += blockDim.x)
+        hist[i] = 0ull;
+    for (int i = tid; i < nwaves * E; i += blockDim.x)
+        cnt[i] = 0;
+    __syncthreads();
+
+    // 1. histogram of every pair, and of the pairs before this block
+    int32_t invalid = 0;
+    const int64_t nvec = a.P / 4;
+    const int4 *v4 = reinterpret_cast<const int4 *>(a.topk_idx);
+#pragma unroll 4
+    for (int64_t i = tid; i < nvec; i += blockDim.x) {
+        const int4 q = v4[i];
+        const int32_t ee[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int32_t e = ee[c];
+            if (e >= 0 && e < E)
+                atomicAdd(&hist[e], 1ull + (4 * i + c < c0 ? (1ull << 32) : 0ull));
+            else if (e != -1)
+                ++invalid;
+        }
+    }
+    for (int64_t q = 4 * nvec + tid; q < a.P; q += blockDim.x) {
+        const int32_t e = a.topk_idx[q];
+        if (e >= 0 && e < E)
+            atomicAdd(&hist[e], 1ull + (q < c0 ? (1ull << 32) : 0ull));
+        else if (e != -1)
+            ++invalid;
+    }
+
+    // 2. rank of the own pair among equal experts in its wave
+    const bool routed = e_own >= 0 && e_own < E;
+    const uint64_t m = match_expert(e_own, routed, a.nbits);
+    const int below = lanes_below(m);
+    if (routed && below == 0)
+        cnt[wave * E + e_own] = __popcll(m);
+    for (int d = kWave / 2; d > 0; d >>= 1)
+        invalid += __shfl_xor(invalid, d);
+    if (lane == 0)
+        red[wave] = invalid;
+    __syncthreads();
+    if (tid == 0)
+        for (int w = 1; w < nwaves; ++w)
+            invalid += red[w];
+
+    // 3. totals; per-wave slot bases start at the pairs of earlier blocks
+    for (int e = tid; e < E; e += blockDim.x) {
+        const unsigned long long h = hist[e];
+        tot[e] = (int32_t)(uint32_t)h;
+        int32_t s = (int32_t)(h >> 32);
+        for (int w = 0; w < nwaves; ++w) {
             const int32_t c = cnt[w * E + e];
             cnt[w * E + e] = s;
             s += c;
@@ -163,110 +464,63 @@ __global__ __launch_bounds__(kBlockThreads) void layout_index(LayoutArgs a)
     }
     __syncthreads();
 
-    // 5. stable slots, rows, and both maps
-    for (int64_t base = q0; base < q1; base += kWave) {
-        const int64_t p = base + lane;
-        const bool in = p < q1;
-        const int32_t e = in ? a.topk_idx[p] : -1;
-        const bool routed = in && e >= 0 && e < E;
-        const uint64_t m = match_expert(e, routed, a.nbits);
-        int32_t row = -1;
-        if (routed) {
-            const int rank = lanes_below(m);
-            const int32_t first = mycnt[e];     // read by every lane of the match ...
-            const int32_t slot = first + rank;
-            if (rank == 0)
-                mycnt[e] = first + __popcll(m);  // ... before its leader advances it
-            if (contiguous)
-                row = off[e] + slot;
-            else if (slot < a.capacity)
-                row = e * a.capacity + slot;
-        }
-        if (in) {
-            a.h.pair_to_row[p] = row;
-            if (row >= 0)
-                a.h.row_to_pair[row] = (int32_t)p;
-        }
+    // 4. segment offsets, then the own pair's row and both maps
+    segment_offsets(a, tot, off, red);
+    if (own) {
+        const int32_t row = routed ? row_of(a, off, e_own, cnt[wave * E + e_own] + below) : -1;
+        a.h.pair_to_row[p] = row;
+        if (row >= 0)
+            a.h.row_to_pair[row] = (int32_t)p;
     }
 
-    // 6. rows that hold no pair: padding of this block's share of experts and
-    //    a slice of the unused tail
-    for (int e = blk; e < E; e += a.nblocks) {
-        const int32_t used = contiguous ? tot[e] : min(tot[e], a.capacity);
-        for (int32_t r = off[e] + used + tid; r < off[e + 1]; r += kBlockThreads)
-            a.h.row_to_pair[r] = -1;
-    }
-    {
-        const int64_t tail0 = off[E];
-        const int64_t span = (a.rows_cap - tail0 + a.nblocks - 1) / a.nblocks;
-        const int64_t r0 = tail0 + (int64_t)blk * span;
-        const int64_t r1 = min((int64_t)a.rows_cap, r0 + span);
-        for (int64_t r = r0 + tid; r < r1; r += kBlockThreads)
-            a.h.row_to_pair[r] = -1;
-    }
-
-    // 7. block 0 publishes counts, offsets and status
-    if (blk == 0) {
-        int32_t overflow = 0;
-        for (int e = tid; e < E; e += kBlockThreads) {
-            a.h.expert_count[e] = tot[e];
-            a.h.recv_count[e] = contiguous ? tot[e] : min(tot[e], a.capacity);
-            a.h.expert_offset[e] = off[e];
-            if (!contiguous)
-                overflow += max(0, tot[e] - a.capacity);
-        }
-        for (int r = tid; r <= a.R; r += kBlockThreads)
-            a.h.rank_offset[r] = off[r * a.L];
-        if (tid == 0)
-            a.h.expert_offset[E] = off[E];
-        int32_t invalid = 0;
-        for (int b = tid; b < table_rows; b += kBlockThreads)
-            invalid += a.ws[(int64_t)b * (E + 1) + E];
-        for (int d = kWave / 2; d > 0; d >>= 1) {
-            overflow += __shfl_xor(overflow, d);
-            invalid += __shfl_xor(invalid, d);
-        }
-        __syncthreads();  // `red` is reused
-        if (lane == 0) {
-            red[wave] = overflow;
-            red[kWavesPerBlock + wave] = invalid;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int32_t o = 0, v = 0;
-            for (int w = 0; w < kWavesPerBlock; ++w) {
-                o += red[w];
-                v += red[kWavesPerBlock + w];
-            }
-            a.h.status[0] = o;
-            a.h.status[1] = v;
-        }
-    }
+    // 5. rows that hold no pair; 6. block 0 publishes
+    fill_unused_rows(a, tot, off);
+    if (blk == 0)
+        publish(a, tot, off, red, invalid);
 }
 
 }  // namespace
 
-LayoutPlan layout_plan(int64_t P)
+// Waves per block: the rank and single kernels keep a [waves][E] int32 table
+// in LDS (at most 32 KiB).
+static int layout_waves(int32_t E) { return E <= 512 ? 16 : (E <= 1024 ? 8 : 4); }
+
+LayoutPlan layout_plan(int64_t P, int32_t E)
 {
-    const int64_t unit = kLayoutChunkUnit;
-    int64_t per = (P + (int64_t)kLayoutMaxBlocks * unit - 1) / ((int64_t)kLayoutMaxBlocks * unit);
-    if (per < 1)
-        per = 1;
     LayoutPlan plan;
-    plan.chunk = (int32_t)(per * unit);
-    int64_t nb = (P + plan.chunk - 1) / plan.chunk;
+    plan.waves = layout_waves(E);
+    plan.single = P <= kSingleMaxPairs && E <= 512;
+    const int64_t per_round = (int64_t)plan.waves * kWave;  // pairs per block per round
+    int64_t rounds = (P + per_round * kLayoutMaxBlocks - 1) / (per_round * kLayoutMaxBlocks);
+    if (rounds < 1 || plan.single)
+        rounds = 1;
+    plan.rounds = (int32_t)rounds;
+    plan.chunk = (int32_t)(per_round * rounds);
+    const int64_t nb = (P + plan.chunk - 1) / plan.chunk;
     plan.nblocks = (int32_t)(nb < 1 ? 1 : nb);
     return plan;
 }
 
-hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream)
+size_t layout_table_bytes(int32_t E)
 {
-    if (a.P > 0) {
-        const size_t lds = sizeof(int32_t) * (size_t)(a.E + 1);
-        hipLaunchKernelGGL(layout_count, dim3(a.nblocks), dim3(kBlockThreads), lds, stream, a);
+    const size_t b = sizeof(int32_t) * (size_t)(E + 1) * kLayoutMaxBlocks;
+    return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_t stream)
+{
+    const dim3 grid(a.nblocks), block(plan.waves * kWave);
+    if (plan.single) {
+        const size_t lds = sizeof(int32_t) * (size_t)(2 * a.E + a.E + a.E + 1 + plan.waves * a.E);
+        hipLaunchKernelGGL(layout_single, grid, block, lds, stream, a);
+        return hipGetLastError();
     }
-    const size_t lds = sizeof(int32_t) * (size_t)(7 * a.E + 1);
-    hipLaunchKernelGGL(layout_index, dim3(a.nblocks), dim3(kBlockThreads), lds, stream, a);
+    if (a.P > 0) {
+        const size_t lds = sizeof(int32_t) * (size_t)plan.waves * a.E;
+        hipLaunchKernelGGL(layout_rank, grid, block, lds, stream, a);
+    }
+    const size_t lds = sizeof(int32_t) * (size_t)(3 * a.E + 3);
+    hipLaunchKernelGGL(layout_index, grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ typedef enum {
 typedef struct {
     int32_t max_tokens;  /* per-call token cap (>= 0); num_tokens > max_tokens -> MOE_ERR_CAPACITY */
     int32_t hidden;      /* H: channels per token, multiple of 8 (of 128 with FP8) */
-    int32_t num_experts; /* E: routed experts, 1..4096 */
+    int32_t num_experts; /* E: routed experts, 1..2048 */
     int32_t num_topk;    /* K: experts per token, 1..32 ([V2-PR] top-k thread: kNumTopk <= 32) */
     int32_t num_ranks;   /* R: virtual destination ranks, E % R == 0; rank r owns experts [r*E/R, (r+1)*E/R) */
     int32_t layout;      /* moe_layout_t */
@@ -111,7 +111,8 @@ typedef struct {
  * the masked layout.  Returns 0 for an invalid config. */
 size_t moe_rows_capacity(const moe_config_t *cfg);
 
-/* Bytes of device workspace moe_dispatch_layout needs (block histograms).
+/* Bytes of device workspace moe_dispatch_layout needs (block histograms and
+ * per-pair slots).
  * Returns 0 for an invalid config. */
 size_t moe_workspace_bytes(const moe_config_t *cfg);
 
@@ -128,7 +129,7 @@ moe_status_t moe_config_check(const moe_config_t *cfg);
  *              (skipped, counted in status[1]).
  *   handle     every array is written: counts, offsets, both maps, status.
  *   workspace  >= moe_workspace_bytes(cfg) bytes of scratch device memory,
- *              clobbered; workspace_bytes is its size.
+ *              16-byte aligned, clobbered; workspace_bytes is its size.
  *
  * Rows of one expert hold its pairs in ascending pair order (a stable
  * counting sort).  Contiguous: row(p) = expert_offset[e] + slot(p), segments

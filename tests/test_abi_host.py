@@ -72,7 +72,7 @@ def test_size_queries(lib):
              quant=M.QUANT_FP8_UE8M0)
     assert M.moe_rows_capacity(c) == 8192 * 8 + 256 * 127
     ws = M.moe_workspace_bytes(c)
-    assert ws >= 64 * 257 * 4 and ws % 256 == 0
+    assert ws >= 257 * 4 and ws % 256 == 0
     c = _cfg(layout=M.LAYOUT_MASKED, capacity=256, num_experts=256, num_topk=8, num_ranks=8)
     assert M.moe_rows_capacity(c) == 256 * 256
     assert M.moe_rows_capacity(_cfg(num_topk=0)) == 0
@@ -122,6 +122,7 @@ def test_layout_argument_errors(lib):
     assert _layout(lib, c, 4, idx=None) == M.MOE_ERR_INVALID_ARG
     assert _layout(lib, c, 4, idx=FAKE + 2) == M.MOE_ERR_INVALID_ARG   # misaligned
     assert _layout(lib, c, 4, ws=None) == M.MOE_ERR_INVALID_ARG
+    assert _layout(lib, c, 4, ws=FAKE + 8) == M.MOE_ERR_INVALID_ARG   # table rows are 16-byte vectors
     assert _layout(lib, c, 4, ws_bytes=16) == M.MOE_ERR_CAPACITY
     for f, _ in M.MoeHandle._fields_:
         assert _layout(lib, c, 4, h=_handle(**{f: None})) == M.MOE_ERR_INVALID_ARG, f

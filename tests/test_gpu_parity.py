@@ -222,6 +222,9 @@ SMALL = [
     (9000, 512, 256, 8, 8, W.LAYOUT_CONTIGUOUS, 128, 1, W.QUANT_FP8_UE8M0),  # > 64 layout chunks
     (1, 2048, 128, 8, 8, W.LAYOUT_MASKED, 1, 128, W.QUANT_FP8_F32),       # T = 1
     (64, 8, 4, 4, 4, W.LAYOUT_CONTIGUOUS, 1, 1, W.QUANT_NONE),            # H = 8, E = R
+    (3000, 128, 600, 4, 8, W.LAYOUT_CONTIGUOUS, 2, 1, W.QUANT_FP8_UE8M0),  # E > 512: 8-wave layout blocks
+    (5000, 256, 2048, 6, 16, W.LAYOUT_MASKED, 1, 3, W.QUANT_FP8_F32),     # E = 2048: 4-wave blocks
+    (140000, 8, 64, 8, 8, W.LAYOUT_CONTIGUOUS, 4, 1, W.QUANT_NONE),       # > 1M pairs: multi-tile waves
 ]
 
 
