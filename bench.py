@@ -3,10 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is the whole path over one batch already resident in HBM:
-moe_dispatch_layout (counts, offsets, maps) + moe_dispatch (row permutation
-with fused FP8 quantization) + moe_combine (weighted top-k reduction), all
-through the C ABI on torch's current stream.  The stand-in expert outputs y
+One step is the whole path over one batch already resident in HBM: the
+dispatch layout (counts, offsets, maps) and the row permutation with fused FP8
+quantization -- by default one moe_dispatch_fused call, which infers the
+layout inside dispatch; with --separate, moe_dispatch_layout + moe_dispatch --
+then moe_combine (weighted top-k reduction), all through the C ABI on torch's
+current stream.  The stand-in expert outputs y
 are a separate, pre-generated input (the expert GEMMs are not part of the
 path), so combine reads them cold, as it would after real experts.
 
@@ -60,22 +62,174 @@ def algorithmic_bytes(wl, n_kept):
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
-def kernel_source_hash(name):
-    with open(os.path.join(ROOT, "combine_topk_idx_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def library_hash():
+    """sha256 over every source the library is built from (kernels, launch
+    plans, ABI): counter figures taken on another build are not reused."""
+    h = hashlib.sha256()
+    for sub in (("include",), ("combine_topk_idx_amd", "csrc")):
+        d = os.path.join(ROOT, *sub)
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".h", ".hip")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic(kernel, source, workload):
+def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since."""
+    None when there is none or the library sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)[workload][kernel]
+            rec = json.load(f)
+        if rec.get("library_sha256") != library_hash():
+            return None
+        return rec[workload][kernel]["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash(source):
-        return None
-    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# profile summaries: fold rocprofv3 output of this script into profiles/
+# ---------------------------------------------------------------------------
+
+QUANT_TEMPLATE = {"0": "bf16", "1": "fp8_f32", "2": "fp8_ue8m0"}
+
+
+def short_kernel(name):
+    """'void moe::(anonymous namespace)::dispatch_rows<2>(moe::DispatchArgs)'
+    -> 'dispatch_rows_fp8_ue8m0'."""
+    base = name.split("(moe::")[0].split("::")[-1]
+    if "<" in base:
+        stem, arg = base[:-1].split("<")
+        base = f"{stem}_{QUANT_TEMPLATE.get(arg, arg)}"
+    return base
+
+
+def read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def find_file(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def read_cmd(d, name):
+    try:
+        with open(os.path.join(d, name + ".cmd")) as f:
+            return f.read().strip()
+    except OSError:
+        return "(command not recorded)"
+
+
+def summarize(run_dir, calib_mib):
+    """Write profiles/traffic.json and one Markdown summary per library
+    kernel from a run directory holding: prof_bench/ (kernel trace + stats),
+    pmc_FETCH_SIZE/ and pmc_WRITE_SIZE/ (one counter per run, with a
+    `calib_mib` MiB device copy in the same runs), bench.json (the benchmark
+    line of the same build) and the *.cmd files naming the commands."""
+    with open(os.path.join(run_dir, "bench.json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    wl = W.WORKLOADS[bench["config"]["workload"]]
+    ab = bench["path"]["algorithmic_bytes"]
+    algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"],
+            "layout_rank": None, "layout_index": None}
+    for q in QUANT_TEMPLATE.values():
+        algo[f"dispatch_rows_{q}"] = ab["dispatch"]
+        algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
+
+    stats = read_csv(find_file(os.path.join(run_dir, "prof_bench"), "kernel_stats.csv"))
+    counters = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for row in read_csv(find_file(os.path.join(run_dir, f"pmc_{c}"), "counter_collection.csv")):
+            if row["Counter_Name"] != c:
+                continue
+            key = (row["Kernel_Name"], int(row["Grid_Size"]))
+            counters.setdefault(c, {}).setdefault(key, []).append(float(row["Counter_Value"]))
+    # calibration: the device copy is the copy kernel with the largest grid
+    copies = {k: v for k, v in counters["FETCH_SIZE"].items() if "copyBuffer" in k[0]}
+    ckey = max(copies, key=lambda k: k[1])
+    copy_kib = calib_mib * 1024.0
+    cf, cw = float(np.median(counters["FETCH_SIZE"][ckey])), float(np.median(counters["WRITE_SIZE"][ckey]))
+    fscale, wscale = copy_kib / cf, copy_kib / cw
+
+    traffic = {"library_sha256": library_hash(),
+               "_calibration": {"copy_bytes": calib_mib << 20, "copy_kernel": ckey[0], "copy_grid": ckey[1],
+                                "copy_fetch_kib_median": cf, "copy_write_kib_median": cw,
+                                "fetch_scale": fscale, "write_scale": wscale},
+               wl.name: {}}
+    per_kernel = {}
+    for (name, grid), vals in counters["FETCH_SIZE"].items():
+        if "moe::" not in name:
+            continue
+        short = short_kernel(name)
+        f_kib = float(np.median(vals))
+        w_kib = float(np.median(counters["WRITE_SIZE"].get((name, grid), [float("nan")])))
+        nbytes = (f_kib * fscale + w_kib * wscale) * 1024.0
+        rec = {"kernel": name, "grid": grid, "dispatches": len(vals), "fetch_kib": f_kib,
+               "write_kib": w_kib, "bytes_per_launch": int(round(nbytes)),
+               "algorithmic_bytes": algo.get(short)}
+        if rec["algorithmic_bytes"]:
+            rec["ratio"] = nbytes / rec["algorithmic_bytes"]
+        traffic[wl.name][short] = rec
+        per_kernel[short] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+
+    layout = "contiguous A=%d" % wl.align if wl.layout == W.LAYOUT_CONTIGUOUS else "masked C=%d" % wl.capacity
+    title = (f"T={wl.T}, H={wl.H}, E={wl.E}, top-{wl.K}, {wl.R} virtual ranks, {layout}, "
+             f"{QUANT_NAME[wl.quant]}")
+    trace_cmd = read_cmd(run_dir, "prof_bench")
+    pmc_cmds = [read_cmd(run_dir, "pmc_FETCH_SIZE"), read_cmd(run_dir, "pmc_WRITE_SIZE")]
+    bench_cmd = read_cmd(run_dir, "bench")
+    per_call = bench["path"]
+    for row in stats:
+        name = row["Name"]
+        if "moe::" not in name:
+            continue
+        short = short_kernel(name)
+        avg, mn, mx, sd = (float(row[k]) / 1e3 for k in ("AverageNs", "MinNs", "MaxNs", "StdDev"))
+        lines = [f"# {short} -- {wl.name} ({title})", "",
+                 f"Kernel: `{name}`", "",
+                 "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+                 "Command:", "", "    " + trace_cmd, "",
+                 "| Calls | Average | Min | Max | StdDev |", "|---|---|---|---|---|",
+                 f"| {row['Calls']} | {avg:.1f} us | {mn:.1f} us | {mx:.1f} us | {sd:.2f} us |", ""]
+        a = algo.get(short)
+        if a:
+            lines += [f"Algorithmic bytes per launch: {a:,} B -> {a / (avg * 1e3):,.0f} GB/s at the traced "
+                      f"average ({a / (avg * 1e3) / HBM_PEAK_GBS:.1%} of the 8 TB/s HBM peak).", ""]
+        lines += [f"Benchmark line of the same build (`{bench_cmd}`), HIP events on the launch stream:",
+                  f"step {per_call['event_ms_per_step'] * 1e3:.1f} us, per call "
+                  + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["per_call_ms_mean"].items())
+                  + "; separate calls "
+                  + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["separate_calls_ms_mean"].items())
+                  + ".", ""]
+        rec = per_kernel.get(short)
+        if rec:
+            lines += ["## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", ""]
+            lines += ["    " + c for c in pmc_cmds]
+            lines += ["", f"| Counter | KiB per dispatch (median of {rec['dispatches']}) | Scale | Bytes |",
+                      "|---|---|---|---|",
+                      f"| FETCH_SIZE | {rec['fetch_kib']:,.1f} | x{fscale:.4f} | {rec['fetch_kib'] * fscale * 1024:,.0f} |",
+                      f"| WRITE_SIZE | {rec['write_kib']:,.1f} | x{wscale:.4f} | {rec['write_kib'] * wscale * 1024:,.0f} |",
+                      f"| **total** | | | **{rec['bytes_per_launch']:,}**"
+                      + (f" ({rec['ratio']:.4f} x algorithmic) |" if a else " |"), "",
+                      f"Scale factors: the same runs copy {calib_mib} MiB device to device (kernel "
+                      f"`{ckey[0]}`, grid {ckey[1]}); per {copy_kib:,.0f} KiB moved its FETCH_SIZE reads "
+                      f"{cf:,.1f} KiB and its WRITE_SIZE {cw:,.1f} KiB, so FETCH_SIZE is multiplied by "
+                      f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f}.", ""]
+        with open(os.path.join(ROOT, "profiles", f"{short}_{wl.name}.md"), "w") as f:
+            f.write("\n".join(lines))
+    print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
 
 
 def cpu_baseline(wl, inp, y, max_tokens):
@@ -104,11 +258,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--num-cus", type=int, default=0)
+    ap.add_argument("--separate", action="store_true",
+                    help="time layout and dispatch as two calls instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--calib-copy-mib", type=int, default=1024,
+                    help="size of the plain device copy run after the timed region (copy "
+                         "ceiling, and the counter calibration for --summarize)")
+    ap.add_argument("--summarize", metavar="RUN_DIR",
+                    help="no benchmark: fold the rocprofv3 output in RUN_DIR into profiles/")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.calib_copy_mib)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -122,12 +284,6 @@ def main():
     wl = W.WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: generating inputs")
     inp = W.make_inputs(wl)
-    y = W.expert_outputs(wl, inp) if wl.expert_output == "random" else None
-    if y is None:
-        import oracle
-        h = oracle.dispatch_layout(inp.topk_idx, wl.E, wl.R, wl.layout, wl.align, wl.capacity)
-        y = W.expert_outputs(wl, inp, h["row_to_pair"])
-
     cfg = M.MoeConfig(max_tokens=wl.T, hidden=wl.H, num_experts=wl.E, num_topk=wl.K,
                       num_ranks=wl.R, layout=wl.layout, align=wl.align, capacity=wl.capacity,
                       quant=wl.quant, num_cus=args.num_cus)
@@ -137,65 +293,92 @@ def main():
     d_idx = torch.from_numpy(inp.topk_idx).to(dev)
     d_w = torch.from_numpy(inp.topk_w).to(dev)
     d_x = torch.from_numpy(inp.x.view(np.int16)).to(dev)
+    if wl.expert_output == "random":
+        y = W.expert_outputs(wl, inp)
+    else:  # outputs that follow the rows' experts: take the row map from the library
+        M.moe_dispatch_layout(cfg, wl.T, d_idx, bufs.handle, bufs.workspace)
+        torch.cuda.synchronize()
+        y = W.expert_outputs(wl, inp, bufs.handle.row_to_pair.cpu().numpy())
     d_y = torch.from_numpy(y.view(np.int16)).to(dev)
     d_out = torch.empty((wl.T, wl.H), dtype=torch.int16, device=dev)
     T = wl.T
     stream = torch.cuda.current_stream()
 
-    nev = args.steps
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-          for k in ("layout", "dispatch", "combine")}
+    fused = not args.separate
 
-    def step(i=None):
-        if i is not None:
-            ev["layout"][i].record(stream)
-        M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, stream)
-        if i is not None:
-            ev["dispatch"][i].record(stream)
-        M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, stream)
-        if i is not None:
-            ev["combine"][i].record(stream)
+    def layout_dispatch():
+        if fused:  # the layout is inferred inside the dispatch call
+            M.moe_dispatch_fused(cfg, T, d_idx, d_x, None, bufs.handle, bufs.workspace, bufs.out_x,
+                                 bufs.out_scale, None, stream)
+        else:
+            M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, stream)
+            M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, stream)
+
+    def combine():
         M.moe_combine(cfg, T, d_y, d_w, bufs.handle, d_out, stream)
 
     # warmup
-    log(f"[bench] warmup {args.warmup} steps")
+    log(f"[bench] warmup {args.warmup} steps ({'fused' if fused else 'separate'} dispatch)")
     for _ in range(args.warmup):
-        step()
+        layout_dispatch()
+        combine()
     torch.cuda.synchronize()
 
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-    log(f"[bench] timing {args.steps} steps")
+    # timed region: K steps between two device synchronisations; HIP events on
+    # the launch stream bracket each combine (the dominant kernel)
+    c_beg = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    c_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i)
-        ends[i].record(stream)
+        layout_dispatch()
+        c_beg[i].record(stream)
+        combine()
+        c_end[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
     ms_total = t_start.elapsed_time(t_end)
     ms_step = wall * 1e3 / args.steps
-    per = {"layout": [], "dispatch": [], "combine": []}
-    for i in range(args.steps):
-        per["layout"].append(ev["layout"][i].elapsed_time(ev["dispatch"][i]))
-        per["dispatch"].append(ev["dispatch"][i].elapsed_time(ev["combine"][i]))
-        per["combine"].append(ev["combine"][i].elapsed_time(ends[i]))
-    per_ms = {k: float(np.mean(v)) for k, v in per.items()}
-    per_med = {k: float(np.median(v)) for k, v in per.items()}
+    combine_ms = [c_beg[i].elapsed_time(c_end[i]) for i in range(args.steps)]
+    dispatch_ms = [t_start.elapsed_time(c_beg[0])] + \
+                  [c_end[i - 1].elapsed_time(c_beg[i]) for i in range(1, args.steps)]
+
+    # after the timed region: the same step as separate calls, each bracketed
+    # by events, for the per-call breakdown
+    n_sep = min(args.steps, 50)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_sep)]
+    for i in range(n_sep):
+        ev[i][0].record(stream)
+        M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, stream)
+        ev[i][1].record(stream)
+        M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, stream)
+        ev[i][2].record(stream)
+        combine()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    sep = {k: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_sep)]))
+           for j, k in enumerate(("layout", "dispatch", "combine"))}
+
+    per_ms = {"layout+dispatch": float(np.mean(dispatch_ms)), "combine": float(np.mean(combine_ms))}
+    per_med = {"layout+dispatch": float(np.median(dispatch_ms)), "combine": float(np.median(combine_ms))}
 
     status = bufs.handle.status.cpu().numpy()
     n_kept = int(bufs.handle.recv_count.cpu().numpy().sum())
     ab = algorithmic_bytes(wl, n_kept)
     total_bytes = sum(ab.values())
-    gbs = {k: ab[k] / (per_ms[k] * 1e-3) / 1e9 for k in ab}
+    gbs = {"layout+dispatch": (ab["layout"] + ab["dispatch"]) / (per_ms["layout+dispatch"] * 1e-3) / 1e9,
+           "combine": ab["combine"] / (per_ms["combine"] * 1e-3) / 1e9}
+    sep_gbs = {k: ab[k] / (sep[k] * 1e-3) / 1e9 for k in ab}
     path_gbs = total_bytes / (ms_step * 1e-3) / 1e9
 
     # attainable ceiling next to it: a plain device copy of 1 GiB
-    n_copy = (args.calib_copy_mib or 1024) * (1 << 20) // 4
+    n_copy = args.calib_copy_mib * (1 << 20) // 4
     src = torch.empty(n_copy, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -210,7 +393,7 @@ def main():
     copy_gbs = 2 * n_copy * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    traffic = measured_traffic("moe_combine", "moe_combine.hip", wl.name)
+    traffic = measured_traffic("combine_kernel", wl.name)
     result = {
         "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), DSV3 shape",
         "value": T / (ms_step * 1e-3),
@@ -233,8 +416,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "combine_kernel",
                      "achieved": gbs["combine"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs["combine"] / HBM_PEAK_GBS, "traffic": traffic},
-        "path": {"algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
+        "path": {"calls": "moe_dispatch_fused + moe_combine" if fused else
+                          "moe_dispatch_layout + moe_dispatch + moe_combine",
+                 "algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
                  "per_call_ms_mean": per_ms, "per_call_ms_median": per_med, "per_call_gbs": gbs,
+                 "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
                  "event_ms_per_step": ms_total / args.steps, "kept_pairs": n_kept,
                  "status": status.tolist(), "copy_ceiling_gbs": copy_gbs},
     }

@@ -93,6 +93,8 @@ def _load():
     lib.moe_dispatch_layout.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [cfgp, i32, P, P, hp, P, P, P, P]
     lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_dispatch_fused.argtypes = [cfgp, i32, P, P, P, hp, P, sz, P, P, P, P]
+    lib.moe_dispatch_fused.restype = ctypes.c_int
     lib.moe_combine.argtypes = [cfgp, i32, P, P, hp, P, P]
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -213,11 +215,7 @@ def moe_dispatch_layout(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def moe_dispatch(cfg: MoeConfig, num_tokens: int, x: torch.Tensor, topk_w: Optional[torch.Tensor],
-                 handle: Handle, out_x: torch.Tensor, out_scale: Optional[torch.Tensor] = None,
-                 out_row_weight: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Permute (and FP8-quantize when cfg.quant says so) bf16 rows x [T, H]."""
-    lib = _load()
+def _dispatch_ptrs(cfg, num_tokens, x, topk_w, out_x, out_scale, out_row_weight):
     rows = moe_rows_capacity(cfg)
     H, K = cfg.hidden, cfg.num_topk
     nb = H // 128
@@ -233,9 +231,32 @@ def moe_dispatch(cfg: MoeConfig, num_tokens: int, x: torch.Tensor, topk_w: Optio
     elif out_scale is not None:
         raise ValueError("out_scale must be None without FP8 quantization")
     rp = _ptr(out_row_weight, 4, rows, "out_row_weight")
+    return xp, wp, op, sp, rp
+
+
+def moe_dispatch(cfg: MoeConfig, num_tokens: int, x: torch.Tensor, topk_w: Optional[torch.Tensor],
+                 handle: Handle, out_x: torch.Tensor, out_scale: Optional[torch.Tensor] = None,
+                 out_row_weight: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Permute (and FP8-quantize when cfg.quant says so) bf16 rows x [T, H]."""
+    lib = _load()
+    xp, wp, op, sp, rp = _dispatch_ptrs(cfg, num_tokens, x, topk_w, out_x, out_scale, out_row_weight)
     _check("moe_dispatch", lib.moe_dispatch(
         ctypes.byref(cfg), int(num_tokens), xp, wp, ctypes.byref(handle.c), op, sp, rp,
         _stream(stream)))
+
+
+def moe_dispatch_fused(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, x: torch.Tensor,
+                       topk_w: Optional[torch.Tensor], handle: Handle, workspace: torch.Tensor,
+                       out_x: torch.Tensor, out_scale: Optional[torch.Tensor] = None,
+                       out_row_weight: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Layout + dispatch in one call (one launch for small batches)."""
+    lib = _load()
+    idx = _ptr(topk_idx, 4, num_tokens * cfg.num_topk, "topk_idx") if num_tokens > 0 else None
+    ws = _ptr(workspace, None, 0, "workspace")
+    xp, wp, op, sp, rp = _dispatch_ptrs(cfg, num_tokens, x, topk_w, out_x, out_scale, out_row_weight)
+    _check("moe_dispatch_fused", lib.moe_dispatch_fused(
+        ctypes.byref(cfg), int(num_tokens), idx, xp, wp, ctypes.byref(handle.c), ws,
+        workspace.numel() * workspace.element_size(), op, sp, rp, _stream(stream)))
 
 
 def moe_combine(cfg: MoeConfig, num_tokens: int, y: torch.Tensor, topk_w: torch.Tensor,

@@ -82,6 +82,86 @@ int bits_for(int32_t E)
 
 moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Validates a layout call and fills its launch arguments.
+moe_status_t prepare_layout(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                            const moe_handle_t *handle, void *workspace, size_t workspace_bytes, LayoutArgs &a,
+                            LayoutPlan &lp)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
+        return st;
+    if ((num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4))) || workspace == nullptr ||
+        !aligned(workspace, 16))
+        return MOE_ERR_INVALID_ARG;
+    const int64_t P = (int64_t)num_tokens * cfg->num_topk;
+    lp = layout_plan(P, cfg->num_experts);
+    const size_t table = layout_table_bytes(cfg->num_experts);
+    if (workspace_bytes < table + sizeof(int32_t) * (size_t)P)
+        return MOE_ERR_CAPACITY;
+    a.topk_idx = topk_idx;
+    a.P = P;
+    a.E = cfg->num_experts;
+    a.R = cfg->num_ranks;
+    a.L = cfg->num_experts / cfg->num_ranks;
+    a.layout = cfg->layout;
+    a.align = cfg->layout == MOE_LAYOUT_CONTIGUOUS ? cfg->align : 1;
+    a.capacity = cfg->layout == MOE_LAYOUT_MASKED ? cfg->capacity : 1;
+    a.rows_cap = (int32_t)rows_capacity64(*cfg);
+    a.nbits = bits_for(cfg->num_experts);
+    a.rounds = lp.rounds;
+    a.chunk = lp.chunk;
+    a.nblocks = lp.nblocks;
+    a.ws = static_cast<int32_t *>(workspace);
+    a.slots = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + table);
+    a.h = *handle;
+    return MOE_OK;
+}
+
+// Validates a dispatch call and fills its launch arguments (plan included
+// when there are tokens).
+moe_status_t prepare_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x, const float *topk_w,
+                              const moe_handle_t *handle, void *out_x, void *out_scale, float *out_row_weight,
+                              DispatchArgs &a)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
+        return st;
+    const bool fp8 = cfg->quant != MOE_QUANT_NONE;
+    if (out_x == nullptr || !aligned(out_x, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 ? (out_scale == nullptr || !aligned(out_scale, 4)) : out_scale != nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (out_row_weight != nullptr && !aligned(out_row_weight, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (out_row_weight != nullptr && num_tokens > 0 && (topk_w == nullptr || !aligned(topk_w, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens > 0 && (x == nullptr || !aligned(x, 16)))
+        return MOE_ERR_INVALID_ARG;
+    a.x = x;
+    a.topk_w = topk_w;
+    a.pair_to_row = handle->pair_to_row;
+    a.out_x = out_x;
+    a.out_scale = out_scale;
+    a.out_row_weight = out_row_weight;
+    a.T = num_tokens;
+    a.K = cfg->num_topk;
+    a.H = cfg->hidden;
+    if (num_tokens > 0)
+        a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus,
+                                kDispatchMinItemsPerToken)
+                     : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus,
+                                kDispatchMinItemsPerToken);
+    return MOE_OK;
+}
+
 }  // namespace
 
 int device_cu_count()
@@ -161,39 +241,11 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens, co
                                  const moe_handle_t *handle, void *workspace, size_t workspace_bytes,
                                  void *stream)
 {
-    moe_status_t st = check_config(cfg);
+    LayoutArgs a;
+    LayoutPlan lp;
+    const moe_status_t st = prepare_layout(cfg, num_tokens, topk_idx, handle, workspace, workspace_bytes, a, lp);
     if (st != MOE_OK)
         return st;
-    if ((st = check_handle(handle)) != MOE_OK)
-        return st;
-    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
-        return st;
-    if ((num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4))) || workspace == nullptr ||
-        !aligned(workspace, 16))
-        return MOE_ERR_INVALID_ARG;
-    const int64_t P = (int64_t)num_tokens * cfg->num_topk;
-    const LayoutPlan lp = layout_plan(P, cfg->num_experts);
-    const size_t table = layout_table_bytes(cfg->num_experts);
-    if (workspace_bytes < table + sizeof(int32_t) * (size_t)P)
-        return MOE_ERR_CAPACITY;
-
-    LayoutArgs a;
-    a.topk_idx = topk_idx;
-    a.P = P;
-    a.E = cfg->num_experts;
-    a.R = cfg->num_ranks;
-    a.L = cfg->num_experts / cfg->num_ranks;
-    a.layout = cfg->layout;
-    a.align = cfg->layout == MOE_LAYOUT_CONTIGUOUS ? cfg->align : 1;
-    a.capacity = cfg->layout == MOE_LAYOUT_MASKED ? cfg->capacity : 1;
-    a.rows_cap = (int32_t)rows_capacity64(*cfg);
-    a.nbits = bits_for(cfg->num_experts);
-    a.rounds = lp.rounds;
-    a.chunk = lp.chunk;
-    a.nblocks = lp.nblocks;
-    a.ws = static_cast<int32_t *>(workspace);
-    a.slots = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + table);
-    a.h = *handle;
     return from_hip(launch_layout(a, lp, static_cast<hipStream_t>(stream)));
 }
 
@@ -201,40 +253,46 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
                           const moe_handle_t *handle, void *out_x, void *out_scale, float *out_row_weight,
                           void *stream)
 {
-    moe_status_t st = check_config(cfg);
+    DispatchArgs a;
+    const moe_status_t st =
+        prepare_dispatch(cfg, num_tokens, x, topk_w, handle, out_x, out_scale, out_row_weight, a);
+    if (st != MOE_OK || num_tokens == 0)
+        return st;
+    return from_hip(launch_dispatch(a, cfg->quant, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                                const uint16_t *x, const float *topk_w, const moe_handle_t *handle,
+                                void *workspace, size_t workspace_bytes, void *out_x, void *out_scale,
+                                float *out_row_weight, void *stream)
+{
+    LayoutArgs la;
+    LayoutPlan lp;
+    DispatchArgs da;
+    moe_status_t st = prepare_layout(cfg, num_tokens, topk_idx, handle, workspace, workspace_bytes, la, lp);
     if (st != MOE_OK)
         return st;
-    if ((st = check_handle(handle)) != MOE_OK)
+    st = prepare_dispatch(cfg, num_tokens, x, topk_w, handle, out_x, out_scale, out_row_weight, da);
+    if (st != MOE_OK)
         return st;
-    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
-        return st;
-    const bool fp8 = cfg->quant != MOE_QUANT_NONE;
-    if (out_x == nullptr || !aligned(out_x, 16))
-        return MOE_ERR_INVALID_ARG;
-    if (fp8 ? (out_scale == nullptr || !aligned(out_scale, 4)) : out_scale != nullptr)
-        return MOE_ERR_INVALID_ARG;
-    if (out_row_weight != nullptr && !aligned(out_row_weight, 4))
-        return MOE_ERR_INVALID_ARG;
-    if (out_row_weight != nullptr && num_tokens > 0 && (topk_w == nullptr || !aligned(topk_w, 4)))
-        return MOE_ERR_INVALID_ARG;
-    if (num_tokens > 0 && (x == nullptr || !aligned(x, 16)))
-        return MOE_ERR_INVALID_ARG;
-    if (num_tokens == 0)
-        return MOE_OK;
-
-    DispatchArgs a;
-    a.x = x;
-    a.topk_w = topk_w;
-    a.pair_to_row = handle->pair_to_row;
-    a.out_x = out_x;
-    a.out_scale = out_scale;
-    a.out_row_weight = out_row_weight;
-    a.T = num_tokens;
-    a.K = cfg->num_topk;
-    a.H = cfg->hidden;
-    a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus)
-                 : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus);
-    return from_hip(launch_dispatch(a, cfg->quant, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    FusedPlan fp;
+    if (fused_plan(num_tokens, cfg->num_topk, cfg->hidden, cfg->num_experts, cfg->quant, cfg->num_cus, fp)) {
+        FusedArgs f;
+        f.lay = la;
+        f.lay.rounds = 1;
+        f.lay.chunk = fp.tokens_per_block * cfg->num_topk;
+        f.lay.nblocks = fp.blocks;
+        f.d = da;
+        f.d.plan = fp.plan;
+        f.tokens_per_block = fp.tokens_per_block;
+        return from_hip(launch_dispatch_fused(f, cfg->quant, s));
+    }
+    // batches the one-launch kernel does not take: the two calls back to back
+    hipError_t e = launch_layout(la, lp, s);
+    if (e == hipSuccess && num_tokens > 0)
+        e = launch_dispatch(da, cfg->quant, s);
+    return from_hip(e);
 }
 
 moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *y, const float *topk_w,

@@ -67,6 +67,22 @@ struct DispatchArgs {
     RowPlan plan;
 };
 
+// One launch for layout + dispatch (small batches): block b owns tokens
+// [b * tokens_per_block, ...) and the pairs of those tokens.
+struct FusedArgs {
+    LayoutArgs lay;            // rounds = 1, chunk = tokens_per_block * K, nblocks = blocks
+    DispatchArgs d;            // plan: per-token items inside a block (grid/n_items unused)
+    int32_t tokens_per_block;
+};
+
+struct FusedPlan {
+    int32_t blocks, tokens_per_block;
+    RowPlan plan;
+};
+
+constexpr int kFusedWaves = 16;         // waves per fused block (one block per compute unit)
+constexpr int kFusedMaxExperts = 512;   // keeps the block's LDS within 32 KiB
+
 struct CombineArgs {
     const uint16_t *y;
     const float *topk_w;
@@ -80,6 +96,8 @@ int device_cu_count();
 RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item,
                  int32_t num_cus, int32_t min_items_per_token = 1);
 hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream);
+bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32_t num_cus, FusedPlan &fp);
+hipError_t launch_dispatch_fused(const FusedArgs &f, int32_t quant, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
 // Columns one wave iteration covers, and how many iterations a wave keeps in
@@ -88,8 +106,9 @@ constexpr int kDispatchBf16Width = kWave * 8;    // 8 bf16 = 16 bytes per lane
 constexpr int kDispatchBf16MaxIters = 16;
 constexpr int kDispatchFp8Width = kWave * 16;    // 16 channels per lane, 8 lanes per block
 constexpr int kDispatchFp8MaxIters = 8;
+constexpr int kDispatchMinItemsPerToken = 8;     // about 1024 columns per item: many short waves
 constexpr int kCombineWidth = kWave * 16;        // two vectors of 8 bf16 per lane
 constexpr int kCombineMaxIters = 64;
-constexpr int kCombineMinItemsPerToken = 2;      // rows split in two: more, shorter waves
+constexpr int kCombineMinItemsPerToken = 8;      // about 1024 columns per item: many short waves
 
 }  // namespace moe

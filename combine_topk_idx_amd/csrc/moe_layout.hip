@@ -29,32 +29,20 @@
 // Both end with the same steps: segment offsets by a block-wide scan, the
 // pair <-> row maps, padding rows filled with -1 (one expert per wave over
 // the grid), and block 0 publishing counts, offsets and status.
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace moe {
 
 namespace {
 
+using dev::fill_unused_rows;
+using dev::lanes_below;
+using dev::match_expert;
+using dev::publish;
+using dev::row_of;
+using dev::segment_offsets;
+
 constexpr int kTileRounds = 16;  // runs of 64 pairs a lane keeps in registers
-
-// Lanes of the wave holding the same routed expert as this lane: one ballot
-// per expert-id bit.  Returns 0 for lanes that are not routed.
-__device__ __forceinline__ uint64_t match_expert(int32_t e, bool routed, int nbits)
-{
-    uint64_t m = __ballot(routed);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-    }
-    return routed ? m : 0ull;
-}
-
-// Number of set bits of m below this lane.
-__device__ __forceinline__ int lanes_below(uint64_t m)
-{
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 // Pair range [w0, w1) of wave `wave` in block `blk`.
 struct WaveRange {
@@ -193,110 +181,6 @@ __global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
     }
 }
 
-// ---- steps shared by both schedules -----------------------------------------
-
-// off[0..E] = segment starts: exclusive scan of align-padded totals
-// (contiguous) or e * capacity (masked).  Block-wide; ends with a barrier.
-__device__ void segment_offsets(const LayoutArgs &a, const int32_t *tot, int32_t *off, int32_t *red)
-{
-    const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    if (a.layout == MOE_LAYOUT_CONTIGUOUS) {
-        const int per = (E + blockDim.x - 1) / blockDim.x;
-        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-        int32_t local = 0;
-        for (int e = e0; e < e1; ++e)
-            local += (tot[e] + a.align - 1) / a.align * a.align;
-        int32_t incl = local;  // inclusive scan over the wave
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int32_t v = __shfl_up(incl, d);
-            if (lane >= d)
-                incl += v;
-        }
-        if (lane == kWave - 1)
-            red[wave] = incl;
-        __syncthreads();
-        int32_t base = 0;
-        for (int w = 0; w < wave; ++w)
-            base += red[w];
-        int32_t run = base + incl - local;
-        for (int e = e0; e < e1; ++e) {
-            off[e] = run;
-            run += (tot[e] + a.align - 1) / a.align * a.align;
-        }
-        if (tid == blockDim.x - 1)
-            off[E] = run;
-    } else {
-        for (int e = tid; e <= E; e += blockDim.x)
-            off[e] = e * a.capacity;
-    }
-    __syncthreads();
-}
-
-// Row of a routed pair of expert e whose slot among e's pairs is s, or -1
-// when it is dropped by the masked capacity.
-__device__ __forceinline__ int32_t row_of(const LayoutArgs &a, const int32_t *off, int32_t e, int32_t s)
-{
-    if (a.layout == MOE_LAYOUT_CONTIGUOUS)
-        return off[e] + s;
-    return s < a.capacity ? e * a.capacity + s : -1;
-}
-
-// row_to_pair = -1 for rows that hold no pair: the padding after each
-// expert's rows (one expert per wave over the grid) and a slice of the tail
-// past the last segment per wave.
-__device__ void fill_unused_rows(const LayoutArgs &a, const int32_t *tot, const int32_t *off)
-{
-    const int lane = threadIdx.x & (kWave - 1), nwaves = blockDim.x / kWave;
-    const int gwave = blockIdx.x * nwaves + (int)(threadIdx.x / kWave);
-    const int gwaves = a.nblocks * nwaves;
-    const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
-    for (int e = gwave; e < a.E; e += gwaves) {
-        const int32_t used = contiguous ? tot[e] : min(tot[e], a.capacity);
-        for (int32_t r = off[e] + used + lane; r < off[e + 1]; r += kWave)
-            a.h.row_to_pair[r] = -1;
-    }
-    const int64_t tail0 = off[a.E];
-    const int64_t span = (a.rows_cap - tail0 + gwaves - 1) / gwaves;
-    const int64_t r0 = tail0 + (int64_t)gwave * span;
-    const int64_t r1 = min((int64_t)a.rows_cap, r0 + span);
-    for (int64_t r = r0 + lane; r < r1; r += kWave)
-        a.h.row_to_pair[r] = -1;
-}
-
-// Block 0 only: counts, offsets, rank offsets and status.  `invalid` is the
-// block's total of invalid ids (valid in thread 0).
-__device__ void publish(const LayoutArgs &a, const int32_t *tot, const int32_t *off, int32_t *red,
-                        int32_t invalid)
-{
-    const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int nwaves = blockDim.x / kWave;
-    const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
-    int32_t overflow = 0;
-    for (int e = tid; e < E; e += blockDim.x) {
-        a.h.expert_count[e] = tot[e];
-        a.h.recv_count[e] = contiguous ? tot[e] : min(tot[e], a.capacity);
-        a.h.expert_offset[e] = off[e];
-        if (!contiguous)
-            overflow += max(0, tot[e] - a.capacity);
-    }
-    for (int r = tid; r <= a.R; r += blockDim.x)
-        a.h.rank_offset[r] = off[r * a.L];
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        overflow += __shfl_xor(overflow, d);
-    __syncthreads();  // `red` is reused
-    if (lane == 0)
-        red[wave] = overflow;
-    __syncthreads();
-    if (tid == 0) {
-        int32_t o = 0;
-        for (int w = 0; w < nwaves; ++w)
-            o += red[w];
-        a.h.expert_offset[E] = off[E];
-        a.h.status[0] = o;
-        a.h.status[1] = invalid;
-    }
-}
-
 // ---- schedule 2: index kernel -------------------------------------------------
 
 __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
@@ -387,96 +271,8 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
 __global__ __launch_bounds__(1024) void layout_single(LayoutArgs a)
 {
     extern __shared__ int32_t lds[];
-    const int E = a.E;
-    unsigned long long *hist = reinterpret_cast<unsigned long long *>(lds);  // [E] low: all, high: earlier blocks
-    int32_t *tot = lds + 2 * E;  // [E]
-    int32_t *off = tot + E;      // [E+1]
-    int32_t *cnt = off + E + 1;  // [WB][E] per-wave counts, then per-wave slot bases
     __shared__ int32_t red[1024 / kWave];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int nwaves = blockDim.x / kWave;
-    const int blk = blockIdx.x;
-    const int64_t c0 = (int64_t)blk * a.chunk;  // one run of 64 pairs per wave
-
-    // own pair, in flight while LDS is cleared
-    const int64_t p = c0 + (int64_t)wave * kWave + lane;
-    const bool own = p < a.P && p < c0 + a.chunk;
-    const int32_t e_own = own ? a.topk_idx[p] : -1;
-    for (int i = tid; i < E; i += blockDim.x)
-        hist[i] = 0ull;
-    for (int i = tid; i < nwaves * E; i += blockDim.x)
-        cnt[i] = 0;
-    __syncthreads();
-
-    // 1. histogram of every pair, and of the pairs before this block
-    int32_t invalid = 0;
-    const int64_t nvec = a.P / 4;
-    const int4 *v4 = reinterpret_cast<const int4 *>(a.topk_idx);
-#pragma unroll 4
-    for (int64_t i = tid; i < nvec; i += blockDim.x) {
-        const int4 q = v4[i];
-        const int32_t ee[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int32_t e = ee[c];
-            if (e >= 0 && e < E)
-                atomicAdd(&hist[e], 1ull + (4 * i + c < c0 ? (1ull << 32) : 0ull));
-            else if (e != -1)
-                ++invalid;
-        }
-    }
-    for (int64_t q = 4 * nvec + tid; q < a.P; q += blockDim.x) {
-        const int32_t e = a.topk_idx[q];
-        if (e >= 0 && e < E)
-            atomicAdd(&hist[e], 1ull + (q < c0 ? (1ull << 32) : 0ull));
-        else if (e != -1)
-            ++invalid;
-    }
-
-    // 2. rank of the own pair among equal experts in its wave
-    const bool routed = e_own >= 0 && e_own < E;
-    const uint64_t m = match_expert(e_own, routed, a.nbits);
-    const int below = lanes_below(m);
-    if (routed && below == 0)
-        cnt[wave * E + e_own] = __popcll(m);
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        invalid += __shfl_xor(invalid, d);
-    if (lane == 0)
-        red[wave] = invalid;
-    __syncthreads();
-    if (tid == 0)
-        for (int w = 1; w < nwaves; ++w)
-            invalid += red[w];
-
-    // 3. totals; per-wave slot bases start at the pairs of earlier blocks
-    for (int e = tid; e < E; e += blockDim.x) {
-        const unsigned long long h = hist[e];
-        tot[e] = (int32_t)(uint32_t)h;
-        int32_t s = (int32_t)(h >> 32);
-        for (int w = 0; w < nwaves; ++w) {
-            const int32_t c = cnt[w * E + e];
-            cnt[w * E + e] = s;
-            s += c;
-        }
-    }
-    __syncthreads();
-
-    // 4. segment offsets, then the own pair's row and both maps
-    segment_offsets(a, tot, off, red);
-    if (own) {
-        const int32_t row = routed ? row_of(a, off, e_own, cnt[wave * E + e_own] + below) : -1;
-        a.h.pair_to_row[p] = row;
-        if (row >= 0)
-            a.h.row_to_pair[row] = (int32_t)p;
-    }
-
-    // 5. rows that hold no pair; 6. block 0 publishes
-    fill_unused_rows(a, tot, off);
-    if (blk == 0)
-        publish(a, tot, off, red, invalid);
+    dev::single_layout_block(a, lds, red, nullptr);
 }
 
 }  // namespace
@@ -511,7 +307,7 @@ hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_
 {
     const dim3 grid(a.nblocks), block(plan.waves * kWave);
     if (plan.single) {
-        const size_t lds = sizeof(int32_t) * (size_t)(2 * a.E + a.E + a.E + 1 + plan.waves * a.E);
+        const size_t lds = sizeof(int32_t) * dev::single_layout_lds_words(a.E, plan.waves);
         hipLaunchKernelGGL(layout_single, grid, block, lds, stream, a);
         return hipGetLastError();
     }

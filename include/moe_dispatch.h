@@ -173,6 +173,25 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
                           void *out_scale, float *out_row_weight, void *stream);
 
 /*
+ * Dispatch with the layout inferred inside the same call, as the V2 dispatch
+ * does ([V2-PR] Motivation and the _dispatch_core commit: no separate layout
+ * pre-pass; counts come back on the handle).  Same arguments, outputs and
+ * errors as moe_dispatch_layout followed by moe_dispatch, and bit-identical
+ * results: the handle is written in full and the dispatched rows, scales and
+ * row weights are those of moe_dispatch.
+ *
+ * For batches of at most 65536 pairs and at most 512 experts it is one
+ * launch: one block per compute unit owns a run of tokens, issues the loads
+ * of its token rows first and builds the layout for its pairs while they are
+ * in flight.  Other batches run the layout and dispatch kernels back to back.
+ * With num_cus > 0 the one-launch form uses that many blocks.
+ */
+moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                                const uint16_t *x, const float *topk_w, const moe_handle_t *handle,
+                                void *workspace, size_t workspace_bytes, void *out_x, void *out_scale,
+                                float *out_row_weight, void *stream);
+
+/*
  * Combine: reduce expert outputs back to token order with the router weights
  * ([VLLM] commit: weighted reduction in combine; [A2A] review: nothing may
  * reduce again afterwards, an extra post-expert reduction double-counts).

@@ -34,7 +34,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"moe_rows_capacity", "moe_workspace_bytes", "moe_config_check",
-                          "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_status_str"}
+                          "moe_dispatch_layout", "moe_dispatch", "moe_dispatch_fused", "moe_combine",
+                          "moe_status_str"}
     out = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
@@ -178,3 +179,30 @@ def test_binding_refuses_host_tensors(lib):
     c = _cfg()
     with pytest.raises(ValueError):
         M._ptr(torch.zeros(4), 4, 0, "t")
+
+
+def _fused(lib, cfg, T, idx=FAKE, x=FAKE, w=None, h=None, ws=FAKE, ws_bytes=1 << 20, out=FAKE, scale=None,
+           rw=None):
+    h = _handle() if h is None else h
+    return lib.moe_dispatch_fused(ctypes.byref(cfg), T, idx, x, w, ctypes.byref(h), ws, ws_bytes, out, scale,
+                                  rw, None)
+
+
+def test_fused_dispatch_argument_errors(lib):
+    """The fused call rejects everything either separate call rejects."""
+    c = _cfg()
+    f8 = _cfg(quant=M.QUANT_FP8_UE8M0)
+    assert _fused(lib, c, 65) == M.MOE_ERR_CAPACITY
+    assert _fused(lib, c, -1) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, idx=None) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, ws=None) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, ws=FAKE + 4) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, ws_bytes=8) == M.MOE_ERR_CAPACITY
+    assert _fused(lib, c, 4, x=None) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, x=FAKE + 8) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, out=None) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, scale=FAKE) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, f8, 4) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, rw=FAKE) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, c, 4, h=_handle(row_to_pair=None)) == M.MOE_ERR_INVALID_ARG
+    assert _fused(lib, _cfg(num_ranks=3), 4) == M.MOE_ERR_INVALID_ARG

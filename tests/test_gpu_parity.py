@@ -69,8 +69,9 @@ def scale_cols(wl):
     return {W.QUANT_NONE: 0, W.QUANT_FP8_F32: nb, W.QUANT_FP8_UE8M0: (nb + 3) // 4}[wl.quant]
 
 
-def run_gpu(wl, idx, w, x, y, cfg):
-    """One layout + dispatch + combine through the ABI; returns host arrays."""
+def run_gpu(wl, idx, w, x, y, cfg, fused=False):
+    """One layout + dispatch + combine through the ABI (layout and dispatch as
+    two calls, or as the one fused call); returns host arrays."""
     T, K, E, R, H = idx.shape[0], wl.K, wl.E, wl.R, wl.H
     rows = M.moe_rows_capacity(cfg)
     handle = M.Handle.__new__(M.Handle)
@@ -94,9 +95,13 @@ def run_gpu(wl, idx, w, x, y, cfg):
     d_w = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
     d_x = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
     d_y = torch.from_numpy(np.ascontiguousarray(y).view(np.int16)).cuda()
-    M.moe_dispatch_layout(cfg, T, d_idx, handle, ws)
-    M.moe_dispatch(cfg, T, d_x, d_w, handle, out_x.view,
-                   out_scale.view if fp8 else None, out_rw.view)
+    if fused:
+        M.moe_dispatch_fused(cfg, T, d_idx, d_x, d_w, handle, ws, out_x.view,
+                             out_scale.view if fp8 else None, out_rw.view)
+    else:
+        M.moe_dispatch_layout(cfg, T, d_idx, handle, ws)
+        M.moe_dispatch(cfg, T, d_x, d_w, handle, out_x.view,
+                       out_scale.view if fp8 else None, out_rw.view)
     M.moe_combine(cfg, T, d_y, d_w, handle, out.view)
     torch.cuda.synchronize()
     res = {n: g.host().view(np.int32) for n, g in bufs.items()}
@@ -158,8 +163,9 @@ def assert_combine_close(g, o, y, w, p2r, K):
     return int(diff.size)
 
 
-def check_parity(wl, idx, w, x, y, cfg, label):
-    g = run_gpu(wl, idx, w, x, y, cfg)
+def check_parity(wl, idx, w, x, y, cfg, label, fused=False):
+    label = f"{label} [{'fused' if fused else 'separate'}]"
+    g = run_gpu(wl, idx, w, x, y, cfg, fused)
     o = run_oracle(wl, idx, w, x, y, cfg)
     for name in ("expert_count", "recv_count", "expert_offset", "rank_offset", "status",
                  "pair_to_row", "row_to_pair"):
@@ -191,17 +197,22 @@ def inputs_for(wl, row_to_pair=None):
 
 # ---- every workload at its full size, in the launch configuration the benchmark times
 
+MODES = [False, True]
+MODE_IDS = ["separate", "fused"]
+
+
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
-def test_workload_full_size(name):
+def test_workload_full_size(name, fused):
     wl = W.WORKLOADS[name]
-    _say(f"full-size workload {name}")
+    _say(f"full-size workload {name} fused={fused}")
     idx, w, x, y = inputs_for(wl)
     cfg = make_cfg(wl)
-    g, o = check_parity(wl, idx, w, x, y, cfg, name)
+    g, o = check_parity(wl, idx, w, x, y, cfg, name, fused)
     if wl.layout == W.LAYOUT_MASKED:
         print(f"[info] {name}: dropped pairs {int(g['status'][0])}", flush=True)
     # determinism: a second run is bitwise identical
-    g2 = run_gpu(wl, idx, w, x, y, cfg)
+    g2 = run_gpu(wl, idx, w, x, y, cfg, fused)
     for k in g:
         if g[k] is not None:
             assert np.array_equal(g[k], g2[k]), f"{name}: {k} not deterministic"
@@ -228,15 +239,16 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("case", SMALL, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_K{c[3]}_L{c[5]}_Q{c[8]}"
                                              for c in SMALL])
-def test_small_ragged(case):
+def test_small_ragged(case, fused):
     T, H, E, K, R, layout, align, cap, quant = case
-    _say(f"small {case}")
+    _say(f"small {case} fused={fused}")
     wl = W.Workload("small", T=T, H=H, E=E, K=K, R=R, layout=layout, align=align,
                     capacity=cap, quant=quant, routing="softmax", seed=1000 + T)
     idx, w, x, y = inputs_for(wl)
-    check_parity(wl, idx, w, x, y, make_cfg(wl), f"small {case}")
+    check_parity(wl, idx, w, x, y, make_cfg(wl), f"small {case}", fused)
 
 
 def _edge_inputs(kind, T, H, E, K, rng):
@@ -264,51 +276,81 @@ def _edge_inputs(kind, T, H, E, K, rng):
     return idx, w, W.f32_to_bf16_bits(xf)
 
 
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("kind", ["one_expert", "invalid_and_unrouted", "duplicates"])
 @pytest.mark.parametrize("layout,quant", [(W.LAYOUT_CONTIGUOUS, W.QUANT_FP8_UE8M0),
                                           (W.LAYOUT_MASKED, W.QUANT_FP8_F32),
                                           (W.LAYOUT_MASKED, W.QUANT_NONE)])
-def test_edge_routing(kind, layout, quant):
+def test_edge_routing(kind, layout, quant, fused):
     T, H, E, K, R = 200, 256, 12, 4, 3
-    _say(f"edge {kind} layout {layout} quant {quant}")
+    _say(f"edge {kind} layout {layout} quant {quant} fused={fused}")
     rng = np.random.default_rng(zlib.crc32(f"{kind}/{layout}/{quant}".encode()))
     wl = W.Workload("edge", T=T, H=H, E=E, K=K, R=R, layout=layout, align=4, capacity=9,
                     quant=quant)
     idx, w, x = _edge_inputs(kind, T, H, E, K, rng)
     y = W.f32_to_bf16_bits(rng.standard_normal((wl.rows_capacity, H)).astype(np.float32))
-    g, o = check_parity(wl, idx, w, x, y, make_cfg(wl), f"edge {kind}")
+    g, o = check_parity(wl, idx, w, x, y, make_cfg(wl), f"edge {kind}", fused)
     if kind == "invalid_and_unrouted":
         assert g["status"][1] > 0
 
 
-def test_capacity_one_masked():
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
+def test_capacity_one_masked(fused):
     T, H, E, K, R = 100, 128, 8, 2, 8
-    _say("masked capacity 1")
+    _say(f"masked capacity 1 fused={fused}")
     wl = W.Workload("cap1", T=T, H=H, E=E, K=K, R=R, layout=W.LAYOUT_MASKED, capacity=1,
                     quant=W.QUANT_FP8_UE8M0, seed=7)
     idx, w, x, y = inputs_for(wl)
-    g, _ = check_parity(wl, idx, w, x, y, make_cfg(wl), "masked capacity 1")
+    g, _ = check_parity(wl, idx, w, x, y, make_cfg(wl), "masked capacity 1", fused)
     assert g["status"][0] == T * K - E
 
 
-def test_fewer_tokens_than_max_and_num_cus():
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
+def test_fewer_tokens_than_max_and_num_cus(fused):
     """A call with num_tokens < max_tokens, and a restricted compute-unit budget."""
     wl = W.WORKLOADS["deepseekv3_decode_T256"].replace(T=200)
-    _say("T=200 of max 256, num_cus=7")
+    _say(f"T=200 of max 256, num_cus=7 fused={fused}")
     idx, w, x, y = inputs_for(wl.replace(T=200))
     cfg = make_cfg(wl, T_max=256, num_cus=7)
-    check_parity(wl, idx, w, x, y, cfg, "T<max, num_cus=7")
+    check_parity(wl, idx, w, x, y, cfg, "T<max, num_cus=7", fused)
 
 
-def test_zero_tokens_layout():
+def test_fused_unaligned_ids():
+    """topk_idx that is only 4-byte aligned takes the scalar histogram path."""
+    wl = W.Workload("unaligned", T=300, H=512, E=32, K=4, R=4, layout=W.LAYOUT_CONTIGUOUS,
+                    align=8, quant=W.QUANT_FP8_UE8M0, seed=31)
+    _say("fused call with topk_idx at a 4-byte offset")
+    idx, w, x, y = inputs_for(wl)
+    cfg = make_cfg(wl)
+    T, K = idx.shape
+    rows = M.moe_rows_capacity(cfg)
+    base = torch.full((T * K + 4,), -1, dtype=torch.int32, device="cuda")
+    base[1:1 + T * K] = torch.from_numpy(idx.reshape(-1)).cuda()
+    d_idx = base[1:1 + T * K]
+    assert d_idx.data_ptr() % 16 != 0
+    b = M.DispatchBuffers(cfg, device="cuda")
+    d_x = torch.from_numpy(x.view(np.int16)).cuda()
+    M.moe_dispatch_fused(cfg, T, d_idx, d_x, None, b.handle, b.workspace, b.out_x, b.out_scale)
+    torch.cuda.synchronize()
+    h = oracle.dispatch_layout(idx, wl.E, wl.R, wl.layout, wl.align, wl.capacity, rows_cap=rows)
+    for k, v in b.handle.tensors().items():
+        assert np.array_equal(v.cpu().numpy()[:h[k].size], h[k]), k
+    ox, osc, _ = oracle.dispatch(x, h["pair_to_row"], K, wl.quant, rows)
+    kept = h["pair_to_row"][h["pair_to_row"] >= 0]
+    assert np.array_equal(b.out_x.cpu().numpy()[kept], ox[kept])
+    assert np.array_equal(b.out_scale.cpu().numpy().view(np.uint32)[kept], osc[kept])
+
+
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
+def test_zero_tokens_layout(fused):
     wl = W.Workload("empty", T=0, H=256, E=16, K=4, R=4, layout=W.LAYOUT_CONTIGUOUS, align=8)
-    _say("zero tokens")
+    _say(f"zero tokens fused={fused}")
     cfg = make_cfg(wl, T_max=50)
     idx = np.zeros((0, 4), np.int32)
     w = np.zeros((0, 4), np.float32)
     x = np.zeros((0, 256), np.uint16)
     y = np.zeros((M.moe_rows_capacity(cfg), 256), np.uint16)
-    g, _ = check_parity(wl, idx, w, x, y, cfg, "zero tokens")
+    g, _ = check_parity(wl, idx, w, x, y, cfg, "zero tokens", fused)
     assert np.all(g["row_to_pair"] == -1) and not g["expert_offset"].any()
 
 
@@ -340,4 +382,4 @@ def test_quant_sweep_all_bf16_magnitudes():
         idx = np.stack([np.arange(T) % 4, (np.arange(T) + 1) % 4], 1).astype(np.int32)
         w = np.full((T, 2), 0.5, np.float32)
         y = W.f32_to_bf16_bits(rng.standard_normal((wl.rows_capacity, H)).astype(np.float32))
-        check_parity(wl, idx, w, x, y, make_cfg(wl), f"sweep quant {quant}")
+        check_parity(wl, idx, w, x, y, make_cfg(wl), f"sweep quant {quant}", fused=True)
