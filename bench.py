@@ -260,6 +260,10 @@ def main():
     ap.add_argument("--num-cus", type=int, default=0)
     ap.add_argument("--separate", action="store_true",
                     help="time layout and dispatch as two calls instead of the fused call")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time graph replays (launch-bound "
+                         "decode batches); per-call times then come from the eager calls after "
+                         "the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -306,48 +310,81 @@ def main():
 
     fused = not args.separate
 
-    def layout_dispatch():
+    def layout_dispatch(st):
         if fused:  # the layout is inferred inside the dispatch call
             M.moe_dispatch_fused(cfg, T, d_idx, d_x, None, bufs.handle, bufs.workspace, bufs.out_x,
-                                 bufs.out_scale, None, stream)
+                                 bufs.out_scale, None, st)
         else:
-            M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, stream)
-            M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, stream)
+            M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, st)
+            M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, st)
 
-    def combine():
-        M.moe_combine(cfg, T, d_y, d_w, bufs.handle, d_out, stream)
+    def combine(st):
+        M.moe_combine(cfg, T, d_y, d_w, bufs.handle, d_out, st)
+
+    def eager_steps(n):
+        """n steps with HIP events on the launch stream around each combine."""
+        beg = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        end = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(n):
+            layout_dispatch(stream)
+            beg[i].record(stream)
+            combine(stream)
+            end[i].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        c_ms = [beg[i].elapsed_time(end[i]) for i in range(n)]
+        d_ms = [t0.elapsed_time(beg[0])] + [end[i - 1].elapsed_time(beg[i]) for i in range(1, n)]
+        return c_ms, d_ms, t0.elapsed_time(t1)
 
     # warmup
-    log(f"[bench] warmup {args.warmup} steps ({'fused' if fused else 'separate'} dispatch)")
+    log(f"[bench] warmup {args.warmup} steps ({'fused' if fused else 'separate'} dispatch"
+        f"{', graph replay' if args.graph else ''})")
     for _ in range(args.warmup):
-        layout_dispatch()
-        combine()
+        layout_dispatch(stream)
+        combine(stream)
     torch.cuda.synchronize()
 
-    # timed region: K steps between two device synchronisations; HIP events on
-    # the launch stream bracket each combine (the dominant kernel)
-    c_beg = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    c_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    graph = None
+    if args.graph:  # one step captured on a side stream, replayed on this one
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layout_dispatch(side)
+            combine(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            layout_dispatch(cap)
+            combine(cap)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: K steps between two device synchronisations; eager steps
+    # carry HIP events on the launch stream around each combine (the dominant
+    # kernel); graph replays are timed as a whole
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        layout_dispatch()
-        c_beg[i].record(stream)
-        combine()
-        c_end[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    if graph is None:
+        combine_ms, dispatch_ms, ms_total = eager_steps(args.steps)
+    else:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_total = t0.elapsed_time(t1)
     wall = time.perf_counter() - wall0
-
-    ms_total = t_start.elapsed_time(t_end)
     ms_step = wall * 1e3 / args.steps
-    combine_ms = [c_beg[i].elapsed_time(c_end[i]) for i in range(args.steps)]
-    dispatch_ms = [t_start.elapsed_time(c_beg[0])] + \
-                  [c_end[i - 1].elapsed_time(c_beg[i]) for i in range(1, args.steps)]
+    if graph is not None:  # per-call times from eager steps after the timed region
+        combine_ms, dispatch_ms, _ = eager_steps(min(args.steps, 50))
 
     # after the timed region: the same step as separate calls, each bracketed
     # by events, for the per-call breakdown
@@ -359,7 +396,7 @@ def main():
         ev[i][1].record(stream)
         M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, stream)
         ev[i][2].record(stream)
-        combine()
+        combine(stream)
         ev[i][3].record(stream)
     torch.cuda.synchronize()
     sep = {k: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_sep)]))
@@ -416,8 +453,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "combine_kernel",
                      "achieved": gbs["combine"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs["combine"] / HBM_PEAK_GBS, "traffic": traffic},
-        "path": {"calls": "moe_dispatch_fused + moe_combine" if fused else
-                          "moe_dispatch_layout + moe_dispatch + moe_combine",
+        "path": {"calls": ("moe_dispatch_fused + moe_combine" if fused else
+                           "moe_dispatch_layout + moe_dispatch + moe_combine")
+                          + (", one HIP graph replay per step" if graph is not None else ""),
                  "algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
                  "per_call_ms_mean": per_ms, "per_call_ms_median": per_med, "per_call_gbs": gbs,
                  "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
