@@ -44,7 +44,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
@@ -56,6 +56,16 @@ def _load():
     lib.oracle_dispatch.restype = None
     lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_combine.restype = None
+    lib.oracle_rank_layout.argtypes = [i32, i32, i32, i32, i64, P, P, P, P, P]
+    lib.oracle_rank_layout.restype = ctypes.c_int
+    lib.oracle_dispatch_dedup.argtypes = [i32, i32, i32, i32, P, P, P, P]
+    lib.oracle_dispatch_dedup.restype = None
+    lib.oracle_expand.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.oracle_expand.restype = None
+    lib.oracle_combine_partial.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_combine_partial.restype = None
+    lib.oracle_combine_reduce.argtypes = [i32, i32, i32, P, P, P]
+    lib.oracle_combine_reduce.restype = None
     for name in ("oracle_bf16_rne_array", "oracle_e4m3_encode_array",
                  "oracle_ue8m0_exponent_array"):
         getattr(lib, name).argtypes = [P, P, i64]
@@ -140,6 +150,103 @@ def combine(y: np.ndarray, topk_w: np.ndarray, pair_to_row: np.ndarray) -> np.nd
     H = y.shape[1]
     out = np.zeros((T, H), np.uint16)
     lib.oracle_combine(T, K, H, _ptr(y), _ptr(w), _ptr(_c(pair_to_row, np.int32)), _ptr(out))
+    return out
+
+
+def _dispatched_buffers(rows, H, quant, out_x, out_scale):
+    NB = H // 128
+    if out_x is None:
+        out_x = np.zeros((rows, H), np.uint16 if quant == QUANT_NONE else np.uint8)
+    if out_scale is None and quant == QUANT_FP8_F32:
+        out_scale = np.zeros((rows, NB), np.float32)
+    if out_scale is None and quant == QUANT_FP8_UE8M0:
+        out_scale = np.zeros((rows, (NB + 3) // 4), np.uint32)
+    for a in (out_x, out_scale):
+        assert a is None or a.flags["C_CONTIGUOUS"]
+    return out_x, out_scale
+
+
+def rank_rows_capacity(T: int, K: int, R: int) -> int:
+    """Rows a per-rank (deduplicated) buffer needs: T * min(K, R)."""
+    return T * min(K, R)
+
+
+def rank_layout(topk_idx: np.ndarray, E: int, R: int, rows_cap: Optional[int] = None) -> dict:
+    """Per-rank token counts, offsets and the (token, rank) <-> row maps."""
+    lib = _load()
+    idx = _c(topk_idx, np.int32)
+    T, K = idx.shape
+    if rows_cap is None:
+        rows_cap = rank_rows_capacity(T, K, R)
+    h = dict(rank_token_count=np.zeros(R, np.int32), rank_token_offset=np.zeros(R + 1, np.int32),
+             token_rank_row=np.zeros(T * R, np.int32), rank_row_to_token=np.zeros(rows_cap, np.int32))
+    rc = lib.oracle_rank_layout(T, K, E, R, rows_cap, _ptr(idx), _ptr(h["rank_token_count"]),
+                                _ptr(h["rank_token_offset"]), _ptr(h["token_rank_row"]),
+                                _ptr(h["rank_row_to_token"]))
+    if rc != 0:
+        raise ValueError("per-rank rows exceed rows_cap")
+    return h
+
+
+def dispatch_dedup(x: np.ndarray, token_rank_row: np.ndarray, R: int, quant: int, rows: int,
+                   out_x: Optional[np.ndarray] = None, out_scale: Optional[np.ndarray] = None):
+    """Each token row (quantized as in dispatch) once per rank it is in.
+    Returns (send_x, send_scale)."""
+    lib = _load()
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    out_x, out_scale = _dispatched_buffers(rows, H, quant, out_x, out_scale)
+    lib.oracle_dispatch_dedup(T, R, H, quant, _ptr(x), _ptr(_c(token_rank_row, np.int32)),
+                              _ptr(out_x), _ptr(out_scale))
+    return out_x, out_scale
+
+
+def expand(topk_idx: np.ndarray, E: int, R: int, quant: int, send_x: np.ndarray,
+           send_scale: Optional[np.ndarray], token_rank_row: np.ndarray,
+           pair_to_row: np.ndarray, rows: int, out_x: Optional[np.ndarray] = None,
+           out_scale: Optional[np.ndarray] = None):
+    """Receive-side expansion of per-rank rows into the per-expert layout.
+    Returns (out_x, out_scale)."""
+    lib = _load()
+    idx = _c(topk_idx, np.int32)
+    T, K = idx.shape
+    send_x = np.ascontiguousarray(send_x)
+    H = send_x.shape[1]
+    out_x, out_scale = _dispatched_buffers(rows, H, quant, out_x, out_scale)
+    ss = None if send_scale is None else np.ascontiguousarray(send_scale)
+    lib.oracle_expand(T, K, E, R, H, quant, _ptr(idx), _ptr(send_x), _ptr(ss),
+                      _ptr(_c(token_rank_row, np.int32)), _ptr(_c(pair_to_row, np.int32)),
+                      _ptr(out_x), _ptr(out_scale))
+    return out_x, out_scale
+
+
+def combine_partial(topk_idx: np.ndarray, E: int, R: int, y: np.ndarray, topk_w: np.ndarray,
+                    pair_to_row: np.ndarray, token_rank_row: np.ndarray, rank_rows: int,
+                    out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-(token, rank) bf16 partial sums [rank_rows, H] (uint16 bits)."""
+    lib = _load()
+    idx = _c(topk_idx, np.int32)
+    T, K = idx.shape
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    if out is None:
+        out = np.zeros((rank_rows, H), np.uint16)
+    assert out.flags["C_CONTIGUOUS"]
+    lib.oracle_combine_partial(T, K, E, R, H, _ptr(idx), _ptr(y), _ptr(_c(topk_w, np.float32)),
+                               _ptr(_c(pair_to_row, np.int32)), _ptr(_c(token_rank_row, np.int32)),
+                               _ptr(out))
+    return out
+
+
+def combine_reduce(partial: np.ndarray, token_rank_row: np.ndarray, R: int) -> np.ndarray:
+    """Sum of a token's per-rank partials in ascending rank: bf16 out [T, H]."""
+    lib = _load()
+    partial = _c(partial, np.uint16)
+    H = partial.shape[1]
+    trr = _c(token_rank_row, np.int32).reshape(-1)
+    T = trr.size // R
+    out = np.zeros((T, H), np.uint16)
+    lib.oracle_combine_reduce(T, R, H, _ptr(partial), _ptr(trr), _ptr(out))
     return out
 
 

@@ -34,6 +34,12 @@
  *     message (weighted reduction in combine); page "[Feature] Add DeepEPv2
  *     (ElasticBuffer) MoE A2A backend", review (extra post-expert reduction
  *     double-counts).
+ *   - The per-rank deduplicated exchange of the V1 dispatch (its layout
+ *     pre-pass, named on page "moe: add DeepEP V2 ElasticBuffer support to MoE
+ *     token dispatcher", Motivation): each token sent once per destination
+ *     rank, expanded to per-expert rows on the receiver, and combined as
+ *     per-rank partial sums reduced again on the source (the multiple-
+ *     reduction option on page vLLM tools/ep_kernels, commit message).
  *
  * The pages leave row order, alignment, overflow handling, scale formulas and
  * rounding open; the readings taken here are listed in the design doc and in the
@@ -420,6 +426,190 @@ void oracle_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y,
                     continue;
                 float prod = topk_w[p] * oracle_bf16_to_float(y[(int64_t)row * H + j]);
                 acc = acc + prod;
+            }
+            out[(int64_t)t * H + j] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-rank deduplicated exchange: send each token once per destination rank */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The per-rank layout that the V1 dispatch computed in a separate pre-pass
+ * (get_dispatch_layout, named on page "moe: add DeepEP V2 ElasticBuffer
+ * support to MoE token dispatcher", Motivation): which ranks each token must
+ * reach and how many tokens each rank receives.  Readings taken here:
+ *   - expert e belongs to rank e / (E/R); token t is in rank r when at least
+ *     one of its pairs has a valid id (0 <= id < E) of rank r.  Ids -1 and
+ *     invalid ids make no rank; a masked-capacity drop on the receiver does
+ *     not change membership (the sender does not know it).
+ *   - rank r's rows are rank_token_offset[r] .. [r+1], its tokens in
+ *     ascending t, with no padding: rank_token_offset is the exclusive scan
+ *     of rank_token_count.
+ *   - token_rank_row[t*R + r] = that row, or -1 when t is not in rank r
+ *     (is_token_in_rank is token_rank_row >= 0); rank_row_to_token[row] = t,
+ *     and -1 for every other row in [0, rank_rows_capacity).
+ * Returns 0, or -1 if the rows exceed rank_rows_capacity.
+ */
+int oracle_rank_layout(int32_t T, int32_t K, int32_t E, int32_t R,
+                       int64_t rank_rows_capacity, const int32_t *topk_idx,
+                       int32_t *rank_token_count, int32_t *rank_token_offset,
+                       int32_t *token_rank_row, int32_t *rank_row_to_token)
+{
+    int32_t L = E / R;
+    for (int32_t r = 0; r < R; r++)
+        rank_token_count[r] = 0;
+    /* membership first: token_rank_row holds 1 / 0 until rows are assigned */
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t r = 0; r < R; r++)
+            token_rank_row[(int64_t)t * R + r] = 0;
+        for (int32_t k = 0; k < K; k++) {
+            int32_t e = topk_idx[(int64_t)t * K + k];
+            if (e >= 0 && e < E)
+                token_rank_row[(int64_t)t * R + e / L] = 1;
+        }
+        for (int32_t r = 0; r < R; r++)
+            rank_token_count[r] += token_rank_row[(int64_t)t * R + r];
+    }
+    rank_token_offset[0] = 0;
+    for (int32_t r = 0; r < R; r++)
+        rank_token_offset[r + 1] = rank_token_offset[r] + rank_token_count[r];
+    if ((int64_t)rank_token_offset[R] > rank_rows_capacity)
+        return -1;
+    for (int64_t row = 0; row < rank_rows_capacity; row++)
+        rank_row_to_token[row] = -1;
+    for (int32_t r = 0; r < R; r++) {
+        int32_t next = rank_token_offset[r];
+        for (int32_t t = 0; t < T; t++) {
+            int32_t *slot = &token_rank_row[(int64_t)t * R + r];
+            if (*slot) {
+                *slot = next;
+                rank_row_to_token[next] = t;
+                next++;
+            } else {
+                *slot = -1;
+            }
+        }
+    }
+    return 0;
+}
+
+/* Bytes of one dispatched row and of its scales, per quant mode. */
+static int64_t row_bytes(int32_t H, int32_t quant)
+{
+    return quant == ORACLE_QUANT_NONE ? 2 * (int64_t)H : (int64_t)H;
+}
+
+static int64_t scale_bytes(int32_t H, int32_t quant)
+{
+    int32_t NB = H / ORACLE_BLOCK;
+    if (quant == ORACLE_QUANT_FP8_F32)
+        return 4 * (int64_t)NB;
+    if (quant == ORACLE_QUANT_FP8_UE8M0)
+        return 4 * (int64_t)((NB + 3) / 4);
+    return 0;
+}
+
+/*
+ * Deduplicated dispatch (sender side): each token's row, quantized as in
+ * oracle_dispatch, is written once per rank it is in, to row
+ * token_rank_row[t*R + r] of the per-rank send buffer.  This is dispatch
+ * with the R (token, rank) slots of a token in place of its K pairs.
+ */
+void oracle_dispatch_dedup(int32_t T, int32_t R, int32_t H, int32_t quant,
+                           const uint16_t *x, const int32_t *token_rank_row,
+                           void *send_x, void *send_scale)
+{
+    oracle_dispatch(T, R, H, quant, x, NULL, token_rank_row, send_x, send_scale, NULL);
+}
+
+/*
+ * Receive-side expansion: every kept pair p = t*K+k of expert e (rank
+ * r = e / (E/R)) gets the bytes of its token's row on rank r:
+ *   out_x[pair_to_row[p], :] = send_x[token_rank_row[t*R + r], :]
+ * and the same for the row's scales.  Other rows are not written.
+ */
+void oracle_expand(int32_t T, int32_t K, int32_t E, int32_t R, int32_t H, int32_t quant,
+                   const int32_t *topk_idx, const void *send_x, const void *send_scale,
+                   const int32_t *token_rank_row, const int32_t *pair_to_row,
+                   void *out_x, void *out_scale)
+{
+    int32_t L = E / R;
+    int64_t rb = row_bytes(H, quant), sb = scale_bytes(H, quant);
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t k = 0; k < K; k++) {
+            int64_t p = (int64_t)t * K + k;
+            int32_t row = pair_to_row[p];
+            if (row < 0)
+                continue;
+            int32_t e = topk_idx[p];
+            int32_t src = token_rank_row[(int64_t)t * R + e / L];
+            assert(src >= 0);
+            memcpy((uint8_t *)out_x + row * rb, (const uint8_t *)send_x + src * rb, (size_t)rb);
+            if (sb > 0)
+                memcpy((uint8_t *)out_scale + row * sb, (const uint8_t *)send_scale + src * sb, (size_t)sb);
+        }
+    }
+}
+
+/*
+ * Partial combine (receiver side, before the return trip): for every token t
+ * and rank r it is in,
+ *   partial[token_rank_row[t*R+r], j] = bf16_RNE( sum over k ascending with
+ *       valid id e of rank r and row = pair_to_row[t*K+k] >= 0
+ *       of topk_w[t*K+k] * y[row, j] )
+ * in binary32 from +0, product and sum each rounded.  A (token, rank) whose
+ * pairs were all dropped gives +0.  The pages name the option of a second
+ * reduction (the VLLM_DEEPEP_V2_ALLOW_MULTIPLE_REDUCTION switch on page vLLM
+ * tools/ep_kernels, commit message); the bf16 partial sums are the reading
+ * taken here.
+ */
+void oracle_combine_partial(int32_t T, int32_t K, int32_t E, int32_t R, int32_t H,
+                            const int32_t *topk_idx, const uint16_t *y, const float *topk_w,
+                            const int32_t *pair_to_row, const int32_t *token_rank_row,
+                            uint16_t *partial)
+{
+    int32_t L = E / R;
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t r = 0; r < R; r++) {
+            int32_t dst = token_rank_row[(int64_t)t * R + r];
+            if (dst < 0)
+                continue;
+            for (int32_t j = 0; j < H; j++) {
+                float acc = 0.0f;
+                for (int32_t k = 0; k < K; k++) {
+                    int64_t p = (int64_t)t * K + k;
+                    int32_t e = topk_idx[p];
+                    int32_t row = pair_to_row[p];
+                    if (!(e >= 0 && e < E) || e / L != r || row < 0)
+                        continue;
+                    float prod = topk_w[p] * oracle_bf16_to_float(y[(int64_t)row * H + j]);
+                    acc = acc + prod;
+                }
+                partial[(int64_t)dst * H + j] = oracle_bf16_rne(acc);
+            }
+        }
+    }
+}
+
+/*
+ * Final reduction on the source rank, after the return trip:
+ *   out[t, j] = bf16_RNE( sum over r ascending with q = token_rank_row[t*R+r]
+ *                          >= 0 of partial[q, j] )
+ * in binary32 from +0.  A token in no rank gives +0.
+ */
+void oracle_combine_reduce(int32_t T, int32_t R, int32_t H, const uint16_t *partial,
+                           const int32_t *token_rank_row, uint16_t *out)
+{
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t j = 0; j < H; j++) {
+            float acc = 0.0f;
+            for (int32_t r = 0; r < R; r++) {
+                int32_t q = token_rank_row[(int64_t)t * R + r];
+                if (q >= 0)
+                    acc = acc + oracle_bf16_to_float(partial[(int64_t)q * H + j]);
             }
             out[(int64_t)t * H + j] = oracle_bf16_rne(acc);
         }
