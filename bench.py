@@ -62,6 +62,104 @@ def algorithmic_bytes(wl, n_kept):
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
+def dedup_bytes(wl, n_kept, n_rows):
+    """Algorithmic bytes per call of the per-rank deduplicated path; n_rows =
+    (token, rank) rows."""
+    T, K, H, R = wl.T, wl.K, wl.H, wl.R
+    nb = H // 128
+    if wl.quant == W.QUANT_NONE:
+        row = 2 * H
+    elif wl.quant == W.QUANT_FP8_F32:
+        row = H + 4 * nb
+    else:
+        row = H + 4 * ((nb + 3) // 4)
+    return {"rank_layout": 4 * T * K + 4 * T * R + 4 * n_rows,
+            "layout": 4 * T * K + 4 * T * K + 4 * n_kept,
+            "dispatch_dedup": 2 * T * H + 4 * T * R + n_rows * row,
+            "expand": 12 * T * K + n_rows * row + n_kept * row,
+            "combine_partial": 2 * n_kept * H + 16 * T * K + 2 * n_rows * H,
+            "combine_reduce": 4 * T * R + 2 * n_rows * H + 2 * T * H}
+
+
+def copy_ceiling(mib, dev, stream):
+    """GB/s of a plain device-to-device copy of `mib` MiB (the attainable
+    ceiling next to the kernels; also the counter calibration)."""
+    n_copy = mib * (1 << 20) // 4
+    src = torch.empty(n_copy, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * n_copy * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
+def run_dedup(args, wl, cfg, d_idx, d_w, d_x, d_y, d_out, bufs, stream):
+    """Times one step of the per-rank deduplicated path: per-rank layout,
+    per-expert layout, deduplicated dispatch, expansion, partial combine and
+    the final reduction, with HIP events between the calls."""
+    T = wl.T
+    db = M.DedupBuffers(cfg, device=d_x.device)
+    calls = [
+        ("rank_layout", lambda: M.moe_rank_layout(cfg, T, d_idx, db.handle, stream)),
+        ("layout", lambda: M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, stream)),
+        ("dispatch_dedup", lambda: M.moe_dispatch_dedup(cfg, T, d_x, db.handle, db.send_x, db.send_scale,
+                                                        stream)),
+        ("expand", lambda: M.moe_expand(cfg, T, d_idx, db.send_x, db.send_scale, db.handle, bufs.handle,
+                                        bufs.out_x, bufs.out_scale, stream)),
+        ("combine_partial", lambda: M.moe_combine_partial(cfg, T, d_idx, d_y, d_w, bufs.handle, db.handle,
+                                                          db.partial, stream)),
+        ("combine_reduce", lambda: M.moe_combine_reduce(cfg, T, db.partial, db.handle, d_out, stream)),
+    ]
+    log(f"[bench] per-rank deduplicated path: warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(n)]
+    for row in ev:  # create the events before the timed region
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {n} steps")
+    wall0 = time.perf_counter()
+    for i in range(n):
+        for j, (_, f) in enumerate(calls):
+            ev[i][j].record(stream)
+            f()
+        ev[i][-1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)]))
+          for j, (name, _) in enumerate(calls)}
+    n_kept = int(bufs.handle.recv_count.cpu().numpy().sum())
+    n_rows = int(db.handle.rank_token_offset.cpu().numpy()[-1])
+    ab = dedup_bytes(wl, n_kept, n_rows)
+    gbs = {k: ab[k] / (ms[k] * 1e-3) / 1e9 for k in ab}
+    ms_step = wall * 1e3 / n
+    step_gbs = sum(ab.values()) / (ms_step * 1e-3) / 1e9
+    copy_gbs = copy_ceiling(args.calib_copy_mib, d_x.device, stream)
+    return {
+        "metric": "per-rank deduplicated dispatch+combine tokens/s (one GPU's local steps)",
+        "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hidden": wl.H, "experts": wl.E, "topk": wl.K,
+                   "virtual_ranks": wl.R, "quant": QUANT_NAME[wl.quant]},
+        "library_sha256": library_hash(),
+        "path": {"calls": [c for c, _ in calls], "per_call_ms_mean": ms, "algorithmic_bytes": ab,
+                 "per_call_gbs": gbs, "gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS,
+                 "kept_pairs": n_kept, "rank_rows": n_rows, "copy_ceiling_gbs": copy_gbs,
+                 "event_ms_per_step": float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(n)]))},
+    }
+
+
 def library_hash():
     """sha256 over every source the library is built from (kernels, launch
     plans, ABI): counter figures taken on another build are not reused."""
@@ -76,16 +174,16 @@ def library_hash():
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, section):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the library sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            rec = json.load(f)[section]
         if rec.get("library_sha256") != library_hash():
             return None
-        return rec[workload][kernel]["bytes_per_launch"]
-    except (OSError, KeyError, ValueError):
+        return rec["kernels"][kernel]["bytes_per_launch"]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
 
 
@@ -98,12 +196,31 @@ QUANT_TEMPLATE = {"0": "bf16", "1": "fp8_f32", "2": "fp8_ue8m0"}
 
 def short_kernel(name):
     """'void moe::(anonymous namespace)::dispatch_rows<2>(moe::DispatchArgs)'
-    -> 'dispatch_rows_fp8_ue8m0'."""
+    -> 'dispatch_rows_fp8_ue8m0'; combine_kernel<false> -> 'combine_kernel',
+    combine_kernel<true> -> 'combine_kernel_partial'."""
     base = name.split("(moe::")[0].split("::")[-1]
     if "<" in base:
         stem, arg = base[:-1].split("<")
-        base = f"{stem}_{QUANT_TEMPLATE.get(arg, arg)}"
+        suffix = {"false": "", "true": "_partial"}.get(arg)
+        base = stem + suffix if suffix is not None else f"{stem}_{QUANT_TEMPLATE.get(arg, arg)}"
     return base
+
+
+def kernel_bytes(bench):
+    """Algorithmic bytes per launch of each library kernel a benchmark line ran."""
+    ab = bench["path"]["algorithmic_bytes"]
+    if isinstance(bench["path"]["calls"], list):  # per-rank deduplicated path
+        algo = {"rank_layout_kernel": ab["rank_layout"], "layout_single": ab["layout"],
+                "expand_kernel": ab["expand"], "combine_kernel_partial": ab["combine_partial"],
+                "combine_kernel": ab["combine_reduce"]}
+        for q in QUANT_TEMPLATE.values():
+            algo[f"dispatch_rows_{q}"] = ab["dispatch_dedup"]
+        return algo
+    algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"]}
+    for q in QUANT_TEMPLATE.values():
+        algo[f"dispatch_rows_{q}"] = ab["dispatch"]
+        algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
+    return algo
 
 
 def read_csv(path):
@@ -137,12 +254,12 @@ def summarize(run_dir, calib_mib):
     with open(os.path.join(run_dir, "bench.json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
     wl = W.WORKLOADS[bench["config"]["workload"]]
-    ab = bench["path"]["algorithmic_bytes"]
-    algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"],
-            "layout_rank": None, "layout_index": None}
-    for q in QUANT_TEMPLATE.values():
-        algo[f"dispatch_rows_{q}"] = ab["dispatch"]
-        algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
+    dedup = isinstance(bench["path"]["calls"], list)
+    section = wl.name + (":dedup" if dedup else "")
+    built = bench.get("library_sha256")
+    if built is None:
+        raise SystemExit("bench.json names no library_sha256: rerun the benchmark with this build")
+    algo = kernel_bytes(bench)
 
     stats = read_csv(find_file(os.path.join(run_dir, "prof_bench"), "kernel_stats.csv"))
     counters = {}
@@ -159,11 +276,18 @@ def summarize(run_dir, calib_mib):
     cf, cw = float(np.median(counters["FETCH_SIZE"][ckey])), float(np.median(counters["WRITE_SIZE"][ckey]))
     fscale, wscale = copy_kib / cf, copy_kib / cw
 
-    traffic = {"library_sha256": library_hash(),
-               "_calibration": {"copy_bytes": calib_mib << 20, "copy_kernel": ckey[0], "copy_grid": ckey[1],
-                                "copy_fetch_kib_median": cf, "copy_write_kib_median": cw,
-                                "fetch_scale": fscale, "write_scale": wscale},
-               wl.name: {}}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            traffic = json.load(f)
+    except (OSError, ValueError):
+        traffic = {}
+    traffic = {k: v for k, v in traffic.items() if isinstance(v, dict) and "kernels" in v}
+    traffic[section] = {"library_sha256": built,
+                        "_calibration": {"copy_bytes": calib_mib << 20, "copy_kernel": ckey[0],
+                                         "copy_grid": ckey[1], "copy_fetch_kib_median": cf,
+                                         "copy_write_kib_median": cw, "fetch_scale": fscale,
+                                         "write_scale": wscale},
+                        "kernels": {}}
     per_kernel = {}
     for (name, grid), vals in counters["FETCH_SIZE"].items():
         if "moe::" not in name:
@@ -177,11 +301,11 @@ def summarize(run_dir, calib_mib):
                "algorithmic_bytes": algo.get(short)}
         if rec["algorithmic_bytes"]:
             rec["ratio"] = nbytes / rec["algorithmic_bytes"]
-        traffic[wl.name][short] = rec
+        traffic[section]["kernels"][short] = rec
         per_kernel[short] = rec
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(traffic, f, indent=1)
+        json.dump(dict(sorted(traffic.items())), f, indent=1)
         f.write("\n")
 
     layout = "contiguous A=%d" % wl.align if wl.layout == W.LAYOUT_CONTIGUOUS else "masked C=%d" % wl.capacity
@@ -197,7 +321,7 @@ def summarize(run_dir, calib_mib):
             continue
         short = short_kernel(name)
         avg, mn, mx, sd = (float(row[k]) / 1e3 for k in ("AverageNs", "MinNs", "MaxNs", "StdDev"))
-        lines = [f"# {short} -- {wl.name} ({title})", "",
+        lines = [f"# {short} -- {wl.name}{' (per-rank deduplicated path)' if dedup else ''} ({title})", "",
                  f"Kernel: `{name}`", "",
                  "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
                  "Command:", "", "    " + trace_cmd, "",
@@ -210,8 +334,8 @@ def summarize(run_dir, calib_mib):
         lines += [f"Benchmark line of the same build (`{bench_cmd}`), HIP events on the launch stream:",
                   f"step {per_call['event_ms_per_step'] * 1e3:.1f} us, per call "
                   + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["per_call_ms_mean"].items())
-                  + "; separate calls "
-                  + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["separate_calls_ms_mean"].items())
+                  + ("" if dedup else "; separate calls " + ", ".join(
+                      f"{k} {v * 1e3:.1f} us" for k, v in per_call["separate_calls_ms_mean"].items()))
                   + ".", ""]
         rec = per_kernel.get(short)
         if rec:
@@ -227,7 +351,8 @@ def summarize(run_dir, calib_mib):
                       f"`{ckey[0]}`, grid {ckey[1]}); per {copy_kib:,.0f} KiB moved its FETCH_SIZE reads "
                       f"{cf:,.1f} KiB and its WRITE_SIZE {cw:,.1f} KiB, so FETCH_SIZE is multiplied by "
                       f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f}.", ""]
-        with open(os.path.join(ROOT, "profiles", f"{short}_{wl.name}.md"), "w") as f:
+        fname = f"{short}_{wl.name}{'_dedup_path' if dedup else ''}.md"
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
             f.write("\n".join(lines))
     print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
 
@@ -264,6 +389,9 @@ def main():
                     help="capture one step in a HIP graph and time graph replays (launch-bound "
                          "decode batches); per-call times then come from the eager calls after "
                          "the timed region")
+    ap.add_argument("--dedup", action="store_true",
+                    help="time the per-rank deduplicated path instead (rank layout, dedup dispatch, "
+                         "expansion, partial combine, reduction)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -307,6 +435,9 @@ def main():
     d_out = torch.empty((wl.T, wl.H), dtype=torch.int16, device=dev)
     T = wl.T
     stream = torch.cuda.current_stream()
+    if args.dedup:
+        print(json.dumps(run_dedup(args, wl, cfg, d_idx, d_w, d_x, d_y, d_out, bufs, stream)), flush=True)
+        return
 
     fused = not args.separate
 
@@ -321,22 +452,38 @@ def main():
     def combine(st):
         M.moe_combine(cfg, T, d_y, d_w, bufs.handle, d_out, st)
 
+    enqueue_ms = []  # host time to issue one step, per eager run
+
+    def new_events(n):
+        """n timing events, created (first record) before any timed region."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)
+        torch.cuda.synchronize()
+        return evs
+
     def eager_steps(n):
-        """n steps with HIP events on the launch stream around each combine."""
-        beg = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        end = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        """n steps with HIP events on the launch stream around each combine;
+        returns the combine and layout+dispatch times, the event time of all
+        steps and the wall time between two device synchronisations."""
+        beg, end = new_events(n), new_events(n)
+        t0, t1 = new_events(2)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
         t0.record(stream)
+        h0 = time.perf_counter()
         for i in range(n):
             layout_dispatch(stream)
             beg[i].record(stream)
             combine(stream)
             end[i].record(stream)
         t1.record(stream)
+        enqueue_ms.append((time.perf_counter() - h0) * 1e3 / n)
         torch.cuda.synchronize()
+        wall_s = time.perf_counter() - w0
         c_ms = [beg[i].elapsed_time(end[i]) for i in range(n)]
         d_ms = [t0.elapsed_time(beg[0])] + [end[i - 1].elapsed_time(beg[i]) for i in range(1, n)]
-        return c_ms, d_ms, t0.elapsed_time(t1)
+        return c_ms, d_ms, t0.elapsed_time(t1), wall_s
 
     # warmup
     log(f"[bench] warmup {args.warmup} steps ({'fused' if fused else 'separate'} dispatch"
@@ -369,22 +516,22 @@ def main():
     # carry HIP events on the launch stream around each combine (the dominant
     # kernel); graph replays are timed as a whole
     log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     if graph is None:
-        combine_ms, dispatch_ms, ms_total = eager_steps(args.steps)
+        combine_ms, dispatch_ms, ms_total, wall = eager_steps(args.steps)
     else:
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, t1 = new_events(2)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
         t0.record(stream)
         for _ in range(args.steps):
             graph.replay()
         t1.record(stream)
         torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
         ms_total = t0.elapsed_time(t1)
-    wall = time.perf_counter() - wall0
     ms_step = wall * 1e3 / args.steps
     if graph is not None:  # per-call times from eager steps after the timed region
-        combine_ms, dispatch_ms, _ = eager_steps(min(args.steps, 50))
+        combine_ms, dispatch_ms, _, _ = eager_steps(min(args.steps, 50))
 
     # after the timed region: the same step as separate calls, each bracketed
     # by events, for the per-call breakdown
@@ -414,21 +561,7 @@ def main():
     sep_gbs = {k: ab[k] / (sep[k] * 1e-3) / 1e9 for k in ab}
     path_gbs = total_bytes / (ms_step * 1e-3) / 1e9
 
-    # attainable ceiling next to it: a plain device copy of 1 GiB
-    n_copy = args.calib_copy_mib * (1 << 20) // 4
-    src = torch.empty(n_copy, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    c0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * n_copy * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    copy_gbs = copy_ceiling(args.calib_copy_mib, dev, stream)
 
     traffic = measured_traffic("combine_kernel", wl.name)
     result = {
@@ -450,6 +583,7 @@ def main():
                    "layout": "contiguous" if wl.layout == W.LAYOUT_CONTIGUOUS else "masked",
                    "align": wl.align, "capacity": wl.capacity, "quant": QUANT_NAME[wl.quant],
                    "num_cus": args.num_cus},
+        "library_sha256": library_hash(),
         "roofline": {"bound": "hbm", "kernel": "combine_kernel",
                      "achieved": gbs["combine"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs["combine"] / HBM_PEAK_GBS, "traffic": traffic},
@@ -459,7 +593,8 @@ def main():
                  "algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
                  "per_call_ms_mean": per_ms, "per_call_ms_median": per_med, "per_call_gbs": gbs,
                  "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
-                 "event_ms_per_step": ms_total / args.steps, "kept_pairs": n_kept,
+                 "event_ms_per_step": ms_total / args.steps,
+                 "host_enqueue_ms_per_step": enqueue_ms[0] if enqueue_ms else None, "kept_pairs": n_kept,
                  "status": status.tolist(), "copy_ceiling_gbs": copy_gbs},
     }
     if not args.no_cpu_baseline:

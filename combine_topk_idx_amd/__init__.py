@@ -69,6 +69,13 @@ class MoeHandle(ctypes.Structure):
         "pair_to_row", "row_to_pair", "status")]
 
 
+class MoeRankHandle(ctypes.Structure):
+    """moe_rank_handle_t: device pointers of the per-rank layout arrays."""
+
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "rank_token_count", "rank_token_offset", "token_rank_row", "rank_row_to_token")]
+
+
 _lib = None
 
 
@@ -97,6 +104,19 @@ def _load():
     lib.moe_dispatch_fused.restype = ctypes.c_int
     lib.moe_combine.argtypes = [cfgp, i32, P, P, hp, P, P]
     lib.moe_combine.restype = ctypes.c_int
+    rhp = ctypes.POINTER(MoeRankHandle)
+    lib.moe_rank_rows_capacity.argtypes = [cfgp]
+    lib.moe_rank_rows_capacity.restype = sz
+    lib.moe_rank_layout.argtypes = [cfgp, i32, P, rhp, P]
+    lib.moe_rank_layout.restype = ctypes.c_int
+    lib.moe_dispatch_dedup.argtypes = [cfgp, i32, P, rhp, P, P, P]
+    lib.moe_dispatch_dedup.restype = ctypes.c_int
+    lib.moe_expand.argtypes = [cfgp, i32, P, P, P, rhp, hp, P, P, P]
+    lib.moe_expand.restype = ctypes.c_int
+    lib.moe_combine_partial.argtypes = [cfgp, i32, P, P, P, hp, rhp, P, P]
+    lib.moe_combine_partial.restype = ctypes.c_int
+    lib.moe_combine_reduce.argtypes = [cfgp, i32, P, rhp, P, P]
+    lib.moe_combine_reduce.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -122,6 +142,10 @@ def moe_workspace_bytes(cfg: MoeConfig) -> int:
 
 def moe_config_check(cfg: MoeConfig) -> int:
     return int(_load().moe_config_check(ctypes.byref(cfg)))
+
+
+def moe_rank_rows_capacity(cfg: MoeConfig) -> int:
+    return int(_load().moe_rank_rows_capacity(ctypes.byref(cfg)))
 
 
 # ---- marshalling helpers ----------------------------------------------------
@@ -273,3 +297,140 @@ def moe_combine(cfg: MoeConfig, num_tokens: int, y: torch.Tensor, topk_w: torch.
         op = _ptr(out, 2, num_tokens * H, "out")
     _check("moe_combine", lib.moe_combine(
         ctypes.byref(cfg), int(num_tokens), yp, wp, ctypes.byref(handle.c), op, _stream(stream)))
+
+
+# ---- per-rank deduplicated exchange -------------------------------------------
+
+class RankHandle:
+    """Device arrays of one per-rank layout (moe_rank_handle_t), allocated by torch."""
+
+    def __init__(self, cfg: MoeConfig, device="cuda"):
+        R = cfg.num_ranks
+        rows = moe_rank_rows_capacity(cfg)
+        if rows == 0 and cfg.max_tokens > 0:
+            code = moe_config_check(cfg)
+            raise MoeError("moe_rank_rows_capacity", code if code != MOE_OK else MOE_ERR_UNSUPPORTED)
+        z = lambda n: torch.empty(max(int(n), 1), dtype=torch.int32, device=device)
+        self.rank_token_count = z(R)
+        self.rank_token_offset = z(R + 1)
+        self.token_rank_row = z(cfg.max_tokens * R)
+        self.rank_row_to_token = z(rows)
+        self.c = MoeRankHandle(*(t.data_ptr() for t in (
+            self.rank_token_count, self.rank_token_offset, self.token_rank_row,
+            self.rank_row_to_token)))
+
+    def tensors(self) -> dict:
+        return {k: getattr(self, k) for k in (
+            "rank_token_count", "rank_token_offset", "token_rank_row", "rank_row_to_token")}
+
+
+class DedupBuffers:
+    """Per-rank layout and the per-rank row buffers (send rows, their scales,
+    and bf16 partial sums) sized for a config."""
+
+    def __init__(self, cfg: MoeConfig, device="cuda", partial: bool = True):
+        self.cfg = cfg
+        self.rows = moe_rank_rows_capacity(cfg)
+        self.handle = RankHandle(cfg, device)
+        H = cfg.hidden
+        nb = H // 128
+        n = max(self.rows, 1)
+        if cfg.quant == QUANT_NONE:
+            self.send_x = torch.empty((n, H), dtype=torch.int16, device=device)
+            self.send_scale = None
+        else:
+            self.send_x = torch.empty((n, H), dtype=torch.uint8, device=device)
+            w = nb if cfg.quant == QUANT_FP8_F32 else (nb + 3) // 4
+            dt = torch.float32 if cfg.quant == QUANT_FP8_F32 else torch.int32
+            self.send_scale = torch.empty((n, w), dtype=dt, device=device)
+        self.partial = torch.empty((n, H), dtype=torch.int16, device=device) if partial else None
+
+
+def _scale_ptr(cfg, t, rows, name):
+    nb = cfg.hidden // 128
+    if cfg.quant == QUANT_FP8_F32:
+        return _ptr(t, 4, rows * nb, name)
+    if cfg.quant == QUANT_FP8_UE8M0:
+        return _ptr(t, 4, rows * ((nb + 3) // 4), name)
+    if t is not None:
+        raise ValueError(f"{name} must be None without FP8 quantization")
+    return None
+
+
+def moe_rank_layout(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, rank_handle: RankHandle,
+                    stream=None) -> None:
+    """Tokens per rank and the (token, rank) <-> row maps from topk_idx [T, K]."""
+    lib = _load()
+    idx = _ptr(topk_idx, 4, num_tokens * cfg.num_topk, "topk_idx") if num_tokens > 0 else None
+    _check("moe_rank_layout", lib.moe_rank_layout(
+        ctypes.byref(cfg), int(num_tokens), idx, ctypes.byref(rank_handle.c), _stream(stream)))
+
+
+def moe_dispatch_dedup(cfg: MoeConfig, num_tokens: int, x: torch.Tensor, rank_handle: RankHandle,
+                       send_x: torch.Tensor, send_scale: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """Each token row (quantized as by moe_dispatch) once per rank it is in."""
+    lib = _load()
+    rows = moe_rank_rows_capacity(cfg)
+    H = cfg.hidden
+    xp = _ptr(x, 2, num_tokens * H, "x") if num_tokens > 0 else None
+    ob = 2 if cfg.quant == QUANT_NONE else 1
+    op = _ptr(send_x, None, rows * H * ob // send_x.element_size(), "send_x")
+    sp = _scale_ptr(cfg, send_scale, rows, "send_scale")
+    _check("moe_dispatch_dedup", lib.moe_dispatch_dedup(
+        ctypes.byref(cfg), int(num_tokens), xp, ctypes.byref(rank_handle.c), op, sp, _stream(stream)))
+
+
+def moe_expand(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, send_x: torch.Tensor,
+               send_scale: Optional[torch.Tensor], rank_handle: RankHandle, handle: Handle,
+               out_x: torch.Tensor, out_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Receive-side expansion of per-rank rows into the per-expert layout."""
+    lib = _load()
+    rows, qrows = moe_rows_capacity(cfg), moe_rank_rows_capacity(cfg)
+    H = cfg.hidden
+    ob = 2 if cfg.quant == QUANT_NONE else 1
+    if num_tokens > 0:
+        idx = _ptr(topk_idx, 4, num_tokens * cfg.num_topk, "topk_idx")
+        sx = _ptr(send_x, None, qrows * H * ob // send_x.element_size(), "send_x")
+        ss = _scale_ptr(cfg, send_scale, qrows, "send_scale")
+    else:
+        idx = sx = ss = None
+    op = _ptr(out_x, None, rows * H * ob // out_x.element_size(), "out_x")
+    sp = _scale_ptr(cfg, out_scale, rows, "out_scale")
+    _check("moe_expand", lib.moe_expand(
+        ctypes.byref(cfg), int(num_tokens), idx, sx, ss, ctypes.byref(rank_handle.c),
+        ctypes.byref(handle.c), op, sp, _stream(stream)))
+
+
+def moe_combine_partial(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, y: torch.Tensor,
+                        topk_w: torch.Tensor, handle: Handle, rank_handle: RankHandle,
+                        partial: torch.Tensor, stream=None) -> None:
+    """bf16 partial sums per (token, rank) of the weighted expert outputs."""
+    lib = _load()
+    rows, qrows = moe_rows_capacity(cfg), moe_rank_rows_capacity(cfg)
+    H, K = cfg.hidden, cfg.num_topk
+    if num_tokens == 0:
+        idx = yp = wp = pp = None
+    else:
+        idx = _ptr(topk_idx, 4, num_tokens * K, "topk_idx")
+        yp = _ptr(y, 2, rows * H, "y")
+        wp = _ptr(topk_w, 4, num_tokens * K, "topk_w")
+        pp = _ptr(partial, 2, qrows * H, "partial")
+    _check("moe_combine_partial", lib.moe_combine_partial(
+        ctypes.byref(cfg), int(num_tokens), idx, yp, wp, ctypes.byref(handle.c),
+        ctypes.byref(rank_handle.c), pp, _stream(stream)))
+
+
+def moe_combine_reduce(cfg: MoeConfig, num_tokens: int, partial: torch.Tensor,
+                       rank_handle: RankHandle, out: torch.Tensor, stream=None) -> None:
+    """out[t] = bf16(sum over ranks ascending of the token's partial rows)."""
+    lib = _load()
+    qrows = moe_rank_rows_capacity(cfg)
+    H = cfg.hidden
+    if num_tokens == 0:
+        pp = op = None
+    else:
+        pp = _ptr(partial, 2, qrows * H, "partial")
+        op = _ptr(out, 2, num_tokens * H, "out")
+    _check("moe_combine_reduce", lib.moe_combine_reduce(
+        ctypes.byref(cfg), int(num_tokens), pp, ctypes.byref(rank_handle.c), op, _stream(stream)))

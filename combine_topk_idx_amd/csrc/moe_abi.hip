@@ -63,6 +63,39 @@ moe_status_t check_handle(const moe_handle_t *h)
     return MOE_OK;
 }
 
+moe_status_t check_rank_handle(const moe_rank_handle_t *h)
+{
+    if (h == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    const int32_t *arr[] = {h->rank_token_count, h->rank_token_offset, h->token_rank_row, h->rank_row_to_token};
+    for (const int32_t *p : arr)
+        if (p == nullptr || !aligned(p, 4))
+            return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int64_t rank_rows64(const moe_config_t &c)
+{
+    return (int64_t)c.max_tokens * (c.num_topk < c.num_ranks ? c.num_topk : c.num_ranks);
+}
+
+// Config, token count and rank limit shared by the per-rank calls.
+moe_status_t check_dedup(const moe_config_t *cfg, int32_t num_tokens, const moe_rank_handle_t *rh)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if (cfg->num_ranks > kMaxDedupRanks)
+        return MOE_ERR_UNSUPPORTED;
+    if ((st = check_rank_handle(rh)) != MOE_OK)
+        return st;
+    if (num_tokens < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens > cfg->max_tokens)
+        return MOE_ERR_CAPACITY;
+    return MOE_OK;
+}
+
 moe_status_t check_tokens(const moe_config_t &c, int32_t num_tokens)
 {
     if (num_tokens < 0)
@@ -321,6 +354,171 @@ moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint
     a.H = cfg->hidden;
     a.plan = row_plan(num_tokens, cfg->hidden, kCombineWidth, kCombineMaxIters, cfg->num_cus,
                       kCombineMinItemsPerToken);
+    a.topk_idx = nullptr;
+    a.token_rank_row = nullptr;
+    a.E = a.R = a.L = 0;
+    return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_rank_rows_capacity(const moe_config_t *cfg)
+{
+    if (check_config(cfg) != MOE_OK || cfg->num_ranks > kMaxDedupRanks)
+        return 0;
+    return (size_t)rank_rows64(*cfg);
+}
+
+moe_status_t moe_rank_layout(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                             const moe_rank_handle_t *rank_handle, void *stream)
+{
+    const moe_status_t st = check_dedup(cfg, num_tokens, rank_handle);
+    if (st != MOE_OK)
+        return st;
+    if (num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4)))
+        return MOE_ERR_INVALID_ARG;
+    RankLayoutArgs a;
+    a.topk_idx = topk_idx;
+    a.T = num_tokens;
+    a.K = cfg->num_topk;
+    a.E = cfg->num_experts;
+    a.R = cfg->num_ranks;
+    a.L = cfg->num_experts / cfg->num_ranks;
+    a.rows_cap = (int32_t)rank_rows64(*cfg);
+    a.vec4 = (a.K % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;
+    a.rank_magic = ((1ull << 32) + (uint64_t)a.L - 1) / (uint64_t)a.L;
+    a.h = *rank_handle;
+    rank_layout_plan(num_tokens, a.R, a);
+    return from_hip(launch_rank_layout(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch_dedup(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x,
+                                const moe_rank_handle_t *rank_handle, void *send_x, void *send_scale, void *stream)
+{
+    const moe_status_t st = check_dedup(cfg, num_tokens, rank_handle);
+    if (st != MOE_OK)
+        return st;
+    const bool fp8 = cfg->quant != MOE_QUANT_NONE;
+    if (send_x == nullptr || !aligned(send_x, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 ? (send_scale == nullptr || !aligned(send_scale, 4)) : send_scale != nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens > 0 && (x == nullptr || !aligned(x, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return MOE_OK;
+    // the row kernel of dispatch over (token, rank) slots instead of pairs
+    DispatchArgs a;
+    a.x = x;
+    a.topk_w = nullptr;
+    a.pair_to_row = rank_handle->token_rank_row;
+    a.out_x = send_x;
+    a.out_scale = send_scale;
+    a.out_row_weight = nullptr;
+    a.T = num_tokens;
+    a.K = cfg->num_ranks;
+    a.H = cfg->hidden;
+    a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus,
+                            kDispatchMinItemsPerToken)
+                 : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus,
+                            kDispatchMinItemsPerToken);
+    return from_hip(launch_dispatch(a, cfg->quant, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expand(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx, const void *send_x,
+                        const void *send_scale, const moe_rank_handle_t *rank_handle, const moe_handle_t *handle,
+                        void *out_x, void *out_scale, void *stream)
+{
+    moe_status_t st = check_dedup(cfg, num_tokens, rank_handle);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    const bool fp8 = cfg->quant != MOE_QUANT_NONE;
+    if (out_x == nullptr || !aligned(out_x, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 ? (out_scale == nullptr || !aligned(out_scale, 4)) : out_scale != nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4) || send_x == nullptr ||
+                           !aligned(send_x, 16) || (fp8 && (send_scale == nullptr || !aligned(send_scale, 4)))))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return MOE_OK;
+    const int32_t NB = cfg->hidden / kQuantGroup;
+    ExpandArgs a;
+    a.topk_idx = topk_idx;
+    a.pair_to_row = handle->pair_to_row;
+    a.token_rank_row = rank_handle->token_rank_row;
+    a.send_x = static_cast<const uint8_t *>(send_x);
+    a.send_scale = static_cast<const uint8_t *>(send_scale);
+    a.out_x = static_cast<uint8_t *>(out_x);
+    a.out_scale = static_cast<uint8_t *>(out_scale);
+    a.T = num_tokens;
+    a.K = cfg->num_topk;
+    a.E = cfg->num_experts;
+    a.R = cfg->num_ranks;
+    a.L = cfg->num_experts / cfg->num_ranks;
+    a.row_bytes = fp8 ? cfg->hidden : 2 * cfg->hidden;
+    a.scale_words = cfg->quant == MOE_QUANT_FP8_F32 ? NB : cfg->quant == MOE_QUANT_FP8_UE8M0 ? (NB + 3) / 4 : 0;
+    a.plan = row_plan(num_tokens, a.row_bytes, kExpandWidth, kExpandMaxIters, cfg->num_cus,
+                      kDispatchMinItemsPerToken);
+    return from_hip(launch_expand(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine_partial(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                                 const uint16_t *y, const float *topk_w, const moe_handle_t *handle,
+                                 const moe_rank_handle_t *rank_handle, uint16_t *partial, void *stream)
+{
+    moe_status_t st = check_dedup(cfg, num_tokens, rank_handle);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if (num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4) || y == nullptr || !aligned(y, 16) ||
+                           topk_w == nullptr || !aligned(topk_w, 4) || partial == nullptr || !aligned(partial, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return MOE_OK;
+    CombineArgs a;
+    a.y = y;
+    a.topk_w = topk_w;
+    a.pair_to_row = handle->pair_to_row;
+    a.out = partial;
+    a.T = num_tokens;
+    a.K = cfg->num_topk;
+    a.H = cfg->hidden;
+    a.plan = row_plan(num_tokens, cfg->hidden, kCombineWidth, kCombineMaxIters, cfg->num_cus,
+                      kCombineMinItemsPerToken);
+    a.topk_idx = topk_idx;
+    a.token_rank_row = rank_handle->token_rank_row;
+    a.E = cfg->num_experts;
+    a.R = cfg->num_ranks;
+    a.L = cfg->num_experts / cfg->num_ranks;
+    return from_hip(launch_combine_partial(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine_reduce(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *partial,
+                                const moe_rank_handle_t *rank_handle, uint16_t *out, void *stream)
+{
+    const moe_status_t st = check_dedup(cfg, num_tokens, rank_handle);
+    if (st != MOE_OK)
+        return st;
+    if (num_tokens > 0 && (partial == nullptr || !aligned(partial, 16) || out == nullptr || !aligned(out, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return MOE_OK;
+    // the one-level kernel over (token, rank) rows with unit weights
+    CombineArgs a;
+    a.y = partial;
+    a.topk_w = nullptr;
+    a.pair_to_row = rank_handle->token_rank_row;
+    a.out = out;
+    a.T = num_tokens;
+    a.K = cfg->num_ranks;
+    a.H = cfg->hidden;
+    a.plan = row_plan(num_tokens, cfg->hidden, kCombineWidth, kCombineMaxIters, cfg->num_cus,
+                      kCombineMinItemsPerToken);
+    a.topk_idx = nullptr;
+    a.token_rank_row = nullptr;
+    a.E = a.R = a.L = 0;
     return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 

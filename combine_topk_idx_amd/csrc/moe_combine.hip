@@ -10,6 +10,13 @@
 // kept row (up to 16 in flight per lane), accumulates in ascending k in fp32 with the product
 // and the sum each rounded (no FMA), and stores 8 bf16 (round to nearest even,
 // v_cvt_pk_bf16_f32) as 16-byte vectors.
+//
+// The same kernel serves the two levels of the per-rank deduplicated combine
+// (the multiple-reduction option on page vLLM tools/ep_kernels, commit
+// message).  PARTIAL: the token's pairs are compacted in (rank, k) order and
+// the running sum is stored as one bf16 partial row per (token, rank) each
+// time the rank changes.  The final reduction is the plain kernel over the
+// (token, rank) rows with unit weights.
 #include "moe_internal.h"
 
 namespace moe {
@@ -36,6 +43,26 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+// Stores the bf16 of the sums and clears them.
+__device__ __forceinline__ void store_row(uint16_t *row, const int (&col)[kVecs], const bool (&active)[kVecs],
+                                          float (&acc)[kVecs][8])
+{
+#pragma unroll
+    for (int s = 0; s < kVecs; ++s) {
+        if (active[s]) {
+            uint4 o;
+            o.x = pack_bf16(acc[s][0], acc[s][1]);
+            o.y = pack_bf16(acc[s][2], acc[s][3]);
+            o.z = pack_bf16(acc[s][4], acc[s][5]);
+            o.w = pack_bf16(acc[s][6], acc[s][7]);
+            *reinterpret_cast<uint4 *>(row + col[s]) = o;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[s][e] = 0.0f;
+    }
+}
+
 #pragma clang fp contract(off)
 __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const uint4 &v)
 {
@@ -51,6 +78,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const uint4
     }
 }
 
+template <bool PARTIAL>
 __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -61,16 +89,37 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
         const int t = (int)(item / pl.items_per_token);
         const int c = (int)(item - (int64_t)t * pl.items_per_token);
 
-        // kept rows of the token, compacted in ascending k into lanes 0..n-1
         const int64_t pbase = (int64_t)t * a.K;
         const int32_t r = lane < a.K ? a.pair_to_row[pbase + lane] : -1;
-        const float w = lane < a.K ? a.topk_w[pbase + lane] : 0.0f;
-        const uint64_t kept = __ballot(r >= 0);
-        const int n = __popcll(kept);
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(kept >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)kept, 0u));
-        // kept lanes go to slot `below`; the others park in lanes 32.. (unused)
-        const int dst = r >= 0 ? below : kMaxTopk + (lane & (kMaxTopk - 1));
+        const float w = lane < a.K ? (a.topk_w != nullptr ? a.topk_w[pbase + lane] : 1.0f) : 0.0f;
+        int n, dst;
+        int32_t grp = 0, qrow = 0;
+        if constexpr (!PARTIAL) {
+            // kept rows of the token, compacted in ascending k into lanes 0..n-1
+            const uint64_t kept = __ballot(r >= 0);
+            n = __popcll(kept);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(kept >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)kept, 0u));
+            // kept lanes go to slot `below`; the others park in lanes 32.. (unused)
+            dst = r >= 0 ? below : kMaxTopk + (lane & (kMaxTopk - 1));
+        } else {
+            // pairs with a valid id (kept or dropped), compacted in (rank, k)
+            // order; a dropped pair still opens its rank's partial row
+            const int32_t e = lane < a.K ? a.topk_idx[pbase + lane] : -1;
+            const bool valid = e >= 0 && e < a.E;
+            const int32_t g = valid ? e / a.L : 0;
+            const uint64_t vm = __ballot(valid);
+            n = __popcll(vm);
+            int slot = 0;
+            for (int j = 0; j < a.K; ++j) {
+                const int32_t gj = __builtin_amdgcn_readlane(g, j);
+                slot += (((vm >> j) & 1) && (gj < g || (gj == g && j < lane))) ? 1 : 0;
+            }
+            dst = valid ? slot : kMaxTopk + (lane & (kMaxTopk - 1));
+            const int32_t q = valid ? a.token_rank_row[(int64_t)t * a.R + g] : -1;
+            grp = __builtin_amdgcn_ds_permute(dst * 4, g);
+            qrow = __builtin_amdgcn_ds_permute(dst * 4, q);
+        }
         const int32_t rows = __builtin_amdgcn_ds_permute(dst * 4, r);
         const float wts = __int_as_float(__builtin_amdgcn_ds_permute(dst * 4, __float_as_int(w)));
 
@@ -96,8 +145,9 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
                 uint4 v[kBatch][kVecs];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
-                    if (j0 + j < n) {
-                        const uint16_t *src = a.y + (int64_t)__builtin_amdgcn_readlane(rows, j0 + j) * a.H;
+                    const int32_t rj = __builtin_amdgcn_readlane(rows, j0 + j);
+                    if (j0 + j < n && (!PARTIAL || rj >= 0)) {
+                        const uint16_t *src = a.y + (int64_t)rj * a.H;
 #pragma unroll
                         for (int s = 0; s < kVecs; ++s)
                             if (active[s])
@@ -109,24 +159,27 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
                     if (j0 + j < n) {
                         const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                                         __float_as_int(wts), j0 + j));
+                        if (!PARTIAL || __builtin_amdgcn_readlane(rows, j0 + j) >= 0) {
 #pragma unroll
-                        for (int s = 0; s < kVecs; ++s)
-                            if (active[s])
-                                accumulate(acc[s], wj, v[j][s]);
+                            for (int s = 0; s < kVecs; ++s)
+                                if (active[s])
+                                    accumulate(acc[s], wj, v[j][s]);
+                        }
+                        if constexpr (PARTIAL) {
+                            // the last pair of its rank: store the partial row, restart the sum
+                            const int jj = j0 + j;
+                            const bool last = jj == n - 1 || __builtin_amdgcn_readlane(grp, jj + 1) !=
+                                                                 __builtin_amdgcn_readlane(grp, jj);
+                            if (last) {
+                                uint16_t *prow = a.out + (int64_t)__builtin_amdgcn_readlane(qrow, jj) * a.H;
+                                store_row(prow, col, active, acc);
+                            }
+                        }
                     }
                 }
             }
-#pragma unroll
-            for (int s = 0; s < kVecs; ++s) {
-                if (active[s]) {
-                    uint4 o;
-                    o.x = pack_bf16(acc[s][0], acc[s][1]);
-                    o.y = pack_bf16(acc[s][2], acc[s][3]);
-                    o.z = pack_bf16(acc[s][4], acc[s][5]);
-                    o.w = pack_bf16(acc[s][6], acc[s][7]);
-                    *reinterpret_cast<uint4 *>(outp + col[s]) = o;
-                }
-            }
+            if constexpr (!PARTIAL)
+                store_row(outp, col, active, acc);
         }
     }
 }
@@ -135,7 +188,13 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
     return hipGetLastError();
 }
 

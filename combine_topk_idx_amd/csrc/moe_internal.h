@@ -85,12 +85,51 @@ constexpr int kFusedMaxExperts = 512;   // keeps the block's LDS within 32 KiB
 
 struct CombineArgs {
     const uint16_t *y;
-    const float *topk_w;
+    const float *topk_w;         // NULL: every weight is 1 (the final per-rank reduction)
     const int32_t *pair_to_row;
     uint16_t *out;
     int32_t T, K, H;
     RowPlan plan;
+    // partial combine only: sums per (token, rank) into out rows token_rank_row[t*R + r]
+    const int32_t *topk_idx;
+    const int32_t *token_rank_row;
+    int32_t E, R, L;
 };
+
+// ---- per-rank (deduplicated) exchange --------------------------------------
+
+constexpr int kMaxDedupRanks = 32;     // one bit of a 32-bit mask per rank; lanes 0..R-1 hold ranks
+constexpr int kRankLayoutWaves = 16;
+constexpr int kRankLayoutMaxLdsWords = 8192;  // chunk counts [chunks per block][R]
+constexpr int kRankLayoutMaxCachedTokens = 4096;  // token masks kept in LDS up to this many per block
+
+struct RankLayoutArgs {
+    const int32_t *topk_idx;
+    int32_t T, K, E, R, L;
+    int32_t tokens_per_block;   // multiple of 64
+    int32_t nblocks;
+    int32_t rows_cap;           // rows of rank_row_to_token
+    int32_t vec4;               // K % 4 == 0 and topk_idx 16-byte aligned: ids load as int4
+    uint64_t rank_magic;        // ceil(2^32 / L): e / L = (e * rank_magic) >> 32 for e < 2^21
+    int32_t cache_masks;        // the block's token rank masks stay in LDS between passes
+    moe_rank_handle_t h;
+};
+
+struct ExpandArgs {
+    const int32_t *topk_idx;
+    const int32_t *pair_to_row;
+    const int32_t *token_rank_row;
+    const uint8_t *send_x;
+    const uint8_t *send_scale;
+    uint8_t *out_x;
+    uint8_t *out_scale;
+    int32_t T, K, E, R, L;
+    int32_t row_bytes, scale_words;
+    RowPlan plan;               // over row bytes: kExpandWidth bytes per iteration
+};
+
+constexpr int kExpandWidth = kWave * 16;  // bytes per wave iteration, 16 per lane
+constexpr int kExpandMaxIters = 8;
 
 int device_cu_count();
 RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item,
@@ -99,6 +138,10 @@ hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t str
 bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32_t num_cus, FusedPlan &fp);
 hipError_t launch_dispatch_fused(const FusedArgs &f, int32_t quant, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream);
+bool rank_layout_plan(int32_t T, int32_t R, RankLayoutArgs &a);
+hipError_t launch_rank_layout(const RankLayoutArgs &a, hipStream_t stream);
+hipError_t launch_expand(const ExpandArgs &a, hipStream_t stream);
 
 // Columns one wave iteration covers, and how many iterations a wave keeps in
 // registers at once, per kernel.

@@ -210,6 +210,99 @@ moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint
                          const float *topk_w, const moe_handle_t *handle, uint16_t *out,
                          void *stream);
 
+/* ------------------------------------------------------------------------
+ * Per-rank deduplicated exchange.
+ *
+ * The V1 dispatch first computed a per-rank layout in a separate pre-pass
+ * (get_dispatch_layout, [V2-PR] Motivation) so that a token bound for several
+ * experts of one rank crosses the wire once: the sender writes one row per
+ * (token, destination rank), the receiver expands it to its experts' rows,
+ * and combine returns one partial sum per (token, rank) that the source
+ * reduces again (the multiple-reduction option, [VLLM] commit).  On one GPU
+ * the calls below compute every local step of that exchange; the transfer
+ * itself is not part of the library.  They take num_ranks <= 32 (larger R:
+ * MOE_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+
+/* Per-rank layout: caller-allocated int32 device arrays written by
+ * moe_rank_layout.  Expert e belongs to rank e / (E/R); token t is in rank r
+ * when one of its valid ids (0 <= id < E) belongs to r (-1 and invalid ids
+ * make no rank; masked-capacity drops do not change membership).  Rank r's
+ * rows are rank_token_offset[r] .. [r+1], its tokens in ascending order, with
+ * no padding. */
+typedef struct {
+    int32_t *rank_token_count;  /* [R]   tokens in rank r (num_tokens_per_rank) */
+    int32_t *rank_token_offset; /* [R+1] exclusive scan of rank_token_count */
+    int32_t *token_rank_row;    /* [max_tokens*R] row of (t, r), or -1 when t is not in rank r
+                                   (is_token_in_rank = token_rank_row >= 0) */
+    int32_t *rank_row_to_token; /* [moe_rank_rows_capacity] token of each row, or -1; written in full */
+} moe_rank_handle_t;
+
+/* Rows of the per-rank buffers (send_x, send_scale, partial) and of
+ * rank_row_to_token: max_tokens * min(K, R).  Returns 0 for an invalid config
+ * or num_ranks > 32. */
+size_t moe_rank_rows_capacity(const moe_config_t *cfg);
+
+/*
+ * Per-rank layout from the router's top-k ids (the V1 pre-pass, [V2-PR]
+ * Motivation).  Every array of rank_handle is written; topk_idx as in
+ * moe_dispatch_layout.  No workspace.  num_tokens == 0 is a valid call.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP.
+ */
+moe_status_t moe_rank_layout(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                             const moe_rank_handle_t *rank_handle, void *stream);
+
+/*
+ * Deduplicated dispatch (sender side): each token row, quantized exactly as
+ * moe_dispatch quantizes it (cfg.quant), is written once per rank it is in,
+ * to row token_rank_row[t*R + r] of send_x / send_scale, whose layouts are
+ * those of out_x / out_scale in moe_dispatch with moe_rank_rows_capacity
+ * rows.  Rows holding no (token, rank) are not written.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP.
+ */
+moe_status_t moe_dispatch_dedup(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x,
+                                const moe_rank_handle_t *rank_handle, void *send_x, void *send_scale,
+                                void *stream);
+
+/*
+ * Receive-side expansion: each kept pair p = t*K+k of expert e gets the row
+ * of its token on rank e / (E/R):
+ *   out_x[pair_to_row[p]] = send_x[token_rank_row[t*R + e/(E/R)]]
+ * (bytes of the row and of its scales).  With one source rank the result is
+ * byte-identical to moe_dispatch of the same tokens.  handle is the
+ * per-expert layout of the same topk_idx (moe_dispatch_layout); rows no kept
+ * pair maps to are not written.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP.
+ */
+moe_status_t moe_expand(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                        const void *send_x, const void *send_scale, const moe_rank_handle_t *rank_handle,
+                        const moe_handle_t *handle, void *out_x, void *out_scale, void *stream);
+
+/*
+ * Partial combine (receiver side, before the return trip): for every token t
+ * and rank r it is in,
+ *   partial[token_rank_row[t*R+r], :] = bf16_RNE( sum over k ascending with a
+ *       valid id of rank r and row = pair_to_row[t*K+k] >= 0
+ *       of topk_w[t*K+k] * y[row, :] )
+ * in fp32 from +0, product and sum each rounded; a (token, rank) whose pairs
+ * were all dropped gives +0.  partial is bf16 [moe_rank_rows_capacity, H];
+ * rows holding no (token, rank) are not written.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP.
+ */
+moe_status_t moe_combine_partial(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                                 const uint16_t *y, const float *topk_w, const moe_handle_t *handle,
+                                 const moe_rank_handle_t *rank_handle, uint16_t *partial, void *stream);
+
+/*
+ * Final reduction on the source, after the return trip:
+ *   out[t, :] = bf16_RNE( sum over r ascending with q = token_rank_row[t*R+r]
+ *                          >= 0 of partial[q, :] )
+ * in fp32 from +0; a token in no rank gives +0.  out is bf16 [num_tokens, H].
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP.
+ */
+moe_status_t moe_combine_reduce(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *partial,
+                                const moe_rank_handle_t *rank_handle, uint16_t *out, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *moe_status_str(moe_status_t status);
 

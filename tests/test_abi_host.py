@@ -35,7 +35,9 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"moe_rows_capacity", "moe_workspace_bytes", "moe_config_check",
                           "moe_dispatch_layout", "moe_dispatch", "moe_dispatch_fused", "moe_combine",
-                          "moe_status_str"}
+                          "moe_status_str", "moe_rank_rows_capacity", "moe_rank_layout",
+                          "moe_dispatch_dedup", "moe_expand", "moe_combine_partial",
+                          "moe_combine_reduce"}
     out = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
@@ -206,3 +208,94 @@ def test_fused_dispatch_argument_errors(lib):
     assert _fused(lib, c, 4, rw=FAKE) == M.MOE_ERR_INVALID_ARG
     assert _fused(lib, c, 4, h=_handle(row_to_pair=None)) == M.MOE_ERR_INVALID_ARG
     assert _fused(lib, _cfg(num_ranks=3), 4) == M.MOE_ERR_INVALID_ARG
+
+
+# ---- per-rank deduplicated exchange -------------------------------------------
+
+def _rank_handle(**override):
+    vals = {n: FAKE + 0x100000 + 0x1000 * i for i, (n, _) in enumerate(M.MoeRankHandle._fields_)}
+    vals.update(override)
+    return M.MoeRankHandle(**vals)
+
+
+def test_rank_rows_capacity(lib):
+    c = _cfg(max_tokens=8192, hidden=7168, num_experts=256, num_topk=8, num_ranks=8)
+    assert M.moe_rank_rows_capacity(c) == 8192 * 8
+    assert M.moe_rank_rows_capacity(_cfg(num_topk=6, num_ranks=4, num_experts=8)) == 64 * 4
+    assert M.moe_rank_rows_capacity(_cfg(num_experts=64, num_ranks=64)) == 0   # R > 32
+    assert M.moe_rank_rows_capacity(_cfg(num_ranks=3)) == 0
+    assert lib.moe_rank_rows_capacity(None) == 0
+
+
+def _call(lib, name, cfg, T, **kw):
+    """One per-rank entry point with FAKE arguments, overridable by name.
+    Every use below passes at least one argument the host check rejects (or
+    T == 0 where the call enqueues nothing), so no kernel is ever launched."""
+    a = dict(idx=FAKE, x=FAKE, y=FAKE, w=FAKE, send=FAKE, send_scale=None, out=FAKE, out_scale=None,
+             partial=FAKE, rh=_rank_handle(), h=_handle())
+    a.update(kw)
+    c = ctypes.byref(cfg)
+    rh = None if a["rh"] is None else ctypes.byref(a["rh"])
+    h = ctypes.byref(a["h"])
+    if name == "dispatch_dedup":
+        return lib.moe_dispatch_dedup(c, T, a["x"], rh, a["send"], a["send_scale"], None)
+    if name == "expand":
+        return lib.moe_expand(c, T, a["idx"], a["send"], a["send_scale"], rh, h, a["out"], a["out_scale"], None)
+    if name == "combine_partial":
+        return lib.moe_combine_partial(c, T, a["idx"], a["y"], a["w"], h, rh, a["partial"], None)
+    if name == "combine_reduce":
+        return lib.moe_combine_reduce(c, T, a["partial"], rh, a["out"], None)
+    if name == "rank_layout":
+        return lib.moe_rank_layout(c, T, a["idx"], rh, None)
+    raise KeyError(name)
+
+
+DEDUP = ("dispatch_dedup", "expand", "combine_partial", "combine_reduce", "rank_layout")
+
+
+def test_dedup_argument_errors(lib):
+    c = _cfg()
+    wide = _cfg(num_experts=64, num_ranks=64)
+    for name in DEDUP:
+        assert _call(lib, name, c, 65) == M.MOE_ERR_CAPACITY, name
+        assert _call(lib, name, c, -1) == M.MOE_ERR_INVALID_ARG, name
+        assert _call(lib, name, wide, 4) == M.MOE_ERR_UNSUPPORTED, name
+        assert _call(lib, name, _cfg(num_ranks=3), 4) == M.MOE_ERR_INVALID_ARG, name
+        assert _call(lib, name, c, 4, rh=None) == M.MOE_ERR_INVALID_ARG, name
+        for f, _ in M.MoeRankHandle._fields_:
+            for bad in (None, FAKE + 2):
+                assert _call(lib, name, c, 4, rh=_rank_handle(**{f: bad})) == M.MOE_ERR_INVALID_ARG, (f, name)
+    assert _call(lib, "rank_layout", c, 4, idx=None) == M.MOE_ERR_INVALID_ARG
+    assert _call(lib, "rank_layout", c, 4, idx=FAKE + 2) == M.MOE_ERR_INVALID_ARG
+    # the calls that read the per-expert handle check it too
+    for name in ("expand", "combine_partial"):
+        assert _call(lib, name, c, 4, h=_handle(pair_to_row=None)) == M.MOE_ERR_INVALID_ARG, name
+
+
+def test_dedup_pointer_errors(lib):
+    c = _cfg()
+    f8 = _cfg(quant=M.QUANT_FP8_UE8M0)
+    bad = M.MOE_ERR_INVALID_ARG
+    assert _call(lib, "dispatch_dedup", c, 4, x=None) == bad
+    assert _call(lib, "dispatch_dedup", c, 4, x=FAKE + 8) == bad
+    assert _call(lib, "dispatch_dedup", c, 4, send=FAKE + 8) == bad
+    assert _call(lib, "dispatch_dedup", c, 4, send_scale=FAKE) == bad     # scales without FP8
+    assert _call(lib, "dispatch_dedup", f8, 4) == bad                     # FP8 needs scales
+    assert _call(lib, "expand", c, 4, idx=None) == bad
+    assert _call(lib, "expand", c, 4, send=FAKE + 8) == bad
+    assert _call(lib, "expand", c, 4, out=None) == bad
+    assert _call(lib, "expand", c, 4, out_scale=FAKE) == bad              # scales without FP8
+    assert _call(lib, "expand", f8, 4, out_scale=FAKE) == bad             # FP8 needs send scales
+    assert _call(lib, "expand", f8, 4, send_scale=FAKE) == bad            # ... and out scales
+    assert _call(lib, "combine_partial", c, 4, idx=None) == bad
+    assert _call(lib, "combine_partial", c, 4, y=FAKE + 2) == bad
+    assert _call(lib, "combine_partial", c, 4, w=None) == bad
+    assert _call(lib, "combine_partial", c, 4, partial=FAKE + 2) == bad
+    assert _call(lib, "combine_reduce", c, 4, partial=None) == bad
+    assert _call(lib, "combine_reduce", c, 4, out=FAKE + 2) == bad
+    # zero tokens: valid no-ops that enqueue nothing (the layout call is left
+    # out: with zero tokens it still writes the empty layout on the device)
+    assert _call(lib, "dispatch_dedup", c, 0, x=None) == M.MOE_OK
+    assert _call(lib, "expand", c, 0, idx=None, send=None) == M.MOE_OK
+    assert _call(lib, "combine_partial", c, 0, idx=None, y=None, w=None, partial=None) == M.MOE_OK
+    assert _call(lib, "combine_reduce", c, 0, partial=None, out=None) == M.MOE_OK
