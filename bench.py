@@ -37,7 +37,7 @@ from combine_topk_idx_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
 QUANT_NAME = {W.QUANT_NONE: "bf16", W.QUANT_FP8_F32: "fp8_e4m3_fp32scale",
-              W.QUANT_FP8_UE8M0: "fp8_e4m3_ue8m0"}
+              W.QUANT_FP8_UE8M0: "fp8_e4m3_ue8m0", W.QUANT_MXFP8: "mxfp8_e4m3_e8m0_1x32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -54,6 +54,8 @@ def algorithmic_bytes(wl, n_kept):
         b_elt, scale_row = 2, 0
     elif wl.quant == W.QUANT_FP8_F32:
         b_elt, scale_row = 1, 4 * nb
+    elif wl.quant == W.QUANT_MXFP8:
+        b_elt, scale_row = 1, H // 32
     else:
         b_elt, scale_row = 1, 4 * ((nb + 3) // 4)
     layout = 4 * T * K + 4 * T * K + 4 * n_kept
@@ -71,6 +73,8 @@ def dedup_bytes(wl, n_kept, n_rows):
         row = 2 * H
     elif wl.quant == W.QUANT_FP8_F32:
         row = H + 4 * nb
+    elif wl.quant == W.QUANT_MXFP8:
+        row = H + H // 32
     else:
         row = H + 4 * ((nb + 3) // 4)
     return {"rank_layout": 4 * T * K + 4 * T * R + 4 * n_rows,
@@ -191,7 +195,7 @@ def measured_traffic(kernel, section):
 # profile summaries: fold rocprofv3 output of this script into profiles/
 # ---------------------------------------------------------------------------
 
-QUANT_TEMPLATE = {"0": "bf16", "1": "fp8_f32", "2": "fp8_ue8m0"}
+QUANT_TEMPLATE = {"0": "bf16", "1": "fp8_f32", "2": "fp8_ue8m0", "3": "mxfp8"}
 
 
 def short_kernel(name):

@@ -40,6 +40,7 @@ LAYOUT_MASKED = 1
 QUANT_NONE = 0
 QUANT_FP8_F32 = 1
 QUANT_FP8_UE8M0 = 2
+QUANT_MXFP8 = 3
 
 
 class MoeError(RuntimeError):
@@ -217,10 +218,7 @@ class DispatchBuffers:
         else:
             self.out_x = torch.empty((self.rows, H), dtype=torch.uint8, device=device)
             nb = H // 128
-            if cfg.quant == QUANT_FP8_F32:
-                self.out_scale = torch.empty((self.rows, nb), dtype=torch.float32, device=device)
-            else:
-                self.out_scale = torch.empty((self.rows, (nb + 3) // 4), dtype=torch.int32, device=device)
+            self.out_scale = _scale_buffer(cfg, self.rows, device)
         self.out_row_weight = (torch.empty(self.rows, dtype=torch.float32, device=device)
                                if row_weight else None)
 
@@ -247,13 +245,7 @@ def _dispatch_ptrs(cfg, num_tokens, x, topk_w, out_x, out_scale, out_row_weight)
     wp = _ptr(topk_w, 4, num_tokens * K if out_row_weight is not None else 0, "topk_w")
     ob = 2 if cfg.quant == QUANT_NONE else 1
     op = _ptr(out_x, None, rows * H * ob // out_x.element_size(), "out_x")
-    sp = None
-    if cfg.quant == QUANT_FP8_F32:
-        sp = _ptr(out_scale, 4, rows * nb, "out_scale")
-    elif cfg.quant == QUANT_FP8_UE8M0:
-        sp = _ptr(out_scale, 4, rows * ((nb + 3) // 4), "out_scale")
-    elif out_scale is not None:
-        raise ValueError("out_scale must be None without FP8 quantization")
+    sp = _scale_ptr(cfg, out_scale, rows, "out_scale")
     rp = _ptr(out_row_weight, 4, rows, "out_row_weight")
     return xp, wp, op, sp, rp
 
@@ -340,21 +332,31 @@ class DedupBuffers:
             self.send_scale = None
         else:
             self.send_x = torch.empty((n, H), dtype=torch.uint8, device=device)
-            w = nb if cfg.quant == QUANT_FP8_F32 else (nb + 3) // 4
-            dt = torch.float32 if cfg.quant == QUANT_FP8_F32 else torch.int32
-            self.send_scale = torch.empty((n, w), dtype=dt, device=device)
+            self.send_scale = _scale_buffer(cfg, n, device)
         self.partial = torch.empty((n, H), dtype=torch.int16, device=device) if partial else None
 
 
-def _scale_ptr(cfg, t, rows, name):
+def _scale_layout(cfg):
+    """(dtype, columns) of a row's scales: fp32 per 128 channels, packed UE8M0
+    words (4 blocks each), or MX E8M0 bytes per 32 channels; None for bf16."""
     nb = cfg.hidden // 128
-    if cfg.quant == QUANT_FP8_F32:
-        return _ptr(t, 4, rows * nb, name)
-    if cfg.quant == QUANT_FP8_UE8M0:
-        return _ptr(t, 4, rows * ((nb + 3) // 4), name)
-    if t is not None:
-        raise ValueError(f"{name} must be None without FP8 quantization")
-    return None
+    return {QUANT_FP8_F32: (torch.float32, nb), QUANT_FP8_UE8M0: (torch.int32, (nb + 3) // 4),
+            QUANT_MXFP8: (torch.uint8, cfg.hidden // 32)}.get(cfg.quant)
+
+
+def _scale_buffer(cfg, rows, device):
+    dt, cols = _scale_layout(cfg)
+    return torch.empty((rows, cols), dtype=dt, device=device)
+
+
+def _scale_ptr(cfg, t, rows, name):
+    lay = _scale_layout(cfg)
+    if lay is None:
+        if t is not None:
+            raise ValueError(f"{name} must be None without FP8 quantization")
+        return None
+    dt, cols = lay
+    return _ptr(t, torch.empty(0, dtype=dt).element_size(), rows * cols, name)
 
 
 def moe_rank_layout(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, rank_handle: RankHandle,

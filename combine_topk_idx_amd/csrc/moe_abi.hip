@@ -38,7 +38,8 @@ moe_status_t check_config(const moe_config_t *cfg)
         return MOE_ERR_INVALID_ARG;
     if (c.layout == MOE_LAYOUT_MASKED && c.capacity < 1)
         return MOE_ERR_INVALID_ARG;
-    if (c.quant != MOE_QUANT_NONE && c.quant != MOE_QUANT_FP8_F32 && c.quant != MOE_QUANT_FP8_UE8M0)
+    if (c.quant != MOE_QUANT_NONE && c.quant != MOE_QUANT_FP8_F32 && c.quant != MOE_QUANT_FP8_UE8M0 &&
+        c.quant != MOE_QUANT_MXFP8)
         return MOE_ERR_INVALID_ARG;
     if (c.quant != MOE_QUANT_NONE && c.hidden % kQuantGroup != 0)
         return MOE_ERR_INVALID_ARG;
@@ -457,7 +458,11 @@ moe_status_t moe_expand(const moe_config_t *cfg, int32_t num_tokens, const int32
     a.R = cfg->num_ranks;
     a.L = cfg->num_experts / cfg->num_ranks;
     a.row_bytes = fp8 ? cfg->hidden : 2 * cfg->hidden;
-    a.scale_words = cfg->quant == MOE_QUANT_FP8_F32 ? NB : cfg->quant == MOE_QUANT_FP8_UE8M0 ? (NB + 3) / 4 : 0;
+    // words of scales per row: fp32 per 128 channels, UE8M0 4 blocks per word, MX bytes H/32 = NB words
+    a.scale_words = cfg->quant == MOE_QUANT_FP8_F32     ? NB
+                    : cfg->quant == MOE_QUANT_FP8_UE8M0 ? (NB + 3) / 4
+                    : cfg->quant == MOE_QUANT_MXFP8     ? NB
+                                                        : 0;
     a.plan = row_plan(num_tokens, a.row_bytes, kExpandWidth, kExpandMaxIters, cfg->num_cus,
                       kDispatchMinItemsPerToken);
     return from_hip(launch_expand(a, static_cast<hipStream_t>(stream)));

@@ -336,6 +336,8 @@ __device__ __forceinline__ void load_item(RowRegs<QUANT> &r, const uint16_t *src
 //   fp32 scales: s = a / 448, q = E4M3(clamp(x / s, +-448))
 //   UE8M0:       k = smallest integer with a <= 448 * 2^k, q = E4M3(x * 2^-k),
 //                scale byte k + 127, four blocks per little-endian word.
+// MXFP8 uses 32-channel blocks (OCP MX conversion): a as above, s = floor(log2 a)
+//   - 8, q = E4M3(clamp(x * 2^-s, +-448)), E8M0 byte s + 127, bytes in block order.
 template <int QUANT>
 __device__ __forceinline__ void store_item(const RowRegs<QUANT> &r, const DispatchArgs &a, int it0, int n,
                                            int lane, uint64_t kept, int32_t myrow)
@@ -379,13 +381,27 @@ __device__ __forceinline__ void store_item(const RowRegs<QUANT> &r, const Dispat
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 amax = fmaxf(amax, fabsf(v[j]));
-            amax = max8(amax);
+            // block maximum: 8 lanes for 128-channel blocks, 2 for MX blocks
+            amax = QUANT == MOE_QUANT_MXFP8 ? fmaxf(amax, dpp<0xB1>(amax)) : max8(amax);
             const float af = fmaxf(amax, 1e-10f);
 
             uint4 q;
             float scale_f32 = 0.0f;
             uint32_t scale_byte = 0;
-            if constexpr (QUANT == MOE_QUANT_FP8_UE8M0) {
+            if constexpr (QUANT == MOE_QUANT_MXFP8) {
+                // floor(log2 af) - 8 is the exponent field of af (normal) minus 127 + 8
+                const int sx = (int)(__float_as_uint(af) >> 23) - 135;
+                const float inv = __uint_as_float((uint32_t)(127 - sx) << 23);  // 2^-s, exact
+                scale_byte = (uint32_t)(sx + 127);
+                float d[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    d[j] = fminf(fmaxf(v[j] * inv, -448.0f), 448.0f);
+                q.x = pack_e4m3(d[0], d[1], d[2], d[3]);
+                q.y = pack_e4m3(d[4], d[5], d[6], d[7]);
+                q.z = pack_e4m3(d[8], d[9], d[10], d[11]);
+                q.w = pack_e4m3(d[12], d[13], d[14], d[15]);
+            } else if constexpr (QUANT == MOE_QUANT_FP8_UE8M0) {
                 // smallest k with af <= 448 * 2^k, from the binary32 fields of af
                 // (af >= 1e-10 is normal): af = m * 2^e, 448 = 1.75 * 2^8.
                 const uint32_t ab = __float_as_uint(af);
@@ -418,6 +434,12 @@ __device__ __forceinline__ void store_item(const RowRegs<QUANT> &r, const Dispat
                 word = active && (lane & 7) == 0 ? scale_byte << (8 * (blk & 3)) : 0u;
                 word |= __shfl_xor(word, 8);
                 word |= __shfl_xor(word, 16);
+            } else if (QUANT == MOE_QUANT_MXFP8) {
+                // the 4 MX blocks of a 128-channel group (even lanes 8j..8j+6)
+                // form word `blk` of the row's scale bytes
+                word = active && (lane & 1) == 0 ? scale_byte << (8 * ((lane >> 1) & 3)) : 0u;
+                word |= __shfl_xor(word, 2);
+                word |= __shfl_xor(word, 4);
             }
 
             uint64_t m = kept;
@@ -431,6 +453,9 @@ __device__ __forceinline__ void store_item(const RowRegs<QUANT> &r, const Dispat
                 if (QUANT == MOE_QUANT_FP8_UE8M0) {
                     if (active && (lane & 31) == 0)
                         reinterpret_cast<uint32_t *>(a.out_scale)[(int64_t)row * NW + (blk >> 2)] = word;
+                } else if (QUANT == MOE_QUANT_MXFP8) {
+                    if (active && (lane & 7) == 0)
+                        reinterpret_cast<uint32_t *>(a.out_scale)[(int64_t)row * NB + blk] = word;
                 } else {
                     if (active && (lane & 7) == 0)
                         reinterpret_cast<float *>(a.out_scale)[(int64_t)row * NB + blk] = scale_f32;

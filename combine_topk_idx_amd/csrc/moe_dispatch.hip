@@ -13,7 +13,9 @@
 // kept rows (K full-row 16-byte non-temporal store streams), so skewed routing
 // only changes where rows land.  FP8 lanes hold 16 channels, so one 128-channel block is 8
 // adjacent lanes: the block max is three DPP steps, and one wave iteration
-// covers 8 blocks = two packed UE8M0 words.
+// covers 8 blocks = two packed UE8M0 words.  An MXFP8 block (32 channels, the
+// 1x32 MXFP8 expert format named on page "[Feature] Add DeepEPv2
+// (ElasticBuffer) MoE A2A backend", format check) is two adjacent lanes.
 #include "moe_device.h"
 
 namespace moe {
@@ -101,6 +103,9 @@ hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t str
     case MOE_QUANT_FP8_F32:
         hipLaunchKernelGGL(dispatch_rows<MOE_QUANT_FP8_F32>, grid, block, 0, stream, a);
         break;
+    case MOE_QUANT_MXFP8:
+        hipLaunchKernelGGL(dispatch_rows<MOE_QUANT_MXFP8>, grid, block, 0, stream, a);
+        break;
     default:
         hipLaunchKernelGGL(dispatch_rows<MOE_QUANT_FP8_UE8M0>, grid, block, 0, stream, a);
         break;
@@ -150,6 +155,9 @@ hipError_t launch_dispatch_fused(const FusedArgs &f, int32_t quant, hipStream_t 
         break;
     case MOE_QUANT_FP8_F32:
         hipLaunchKernelGGL(dispatch_fused<MOE_QUANT_FP8_F32>, grid, block, lds, stream, f);
+        break;
+    case MOE_QUANT_MXFP8:
+        hipLaunchKernelGGL(dispatch_fused<MOE_QUANT_MXFP8>, grid, block, lds, stream, f);
         break;
     default:
         hipLaunchKernelGGL(dispatch_fused<MOE_QUANT_FP8_UE8M0>, grid, block, lds, stream, f);

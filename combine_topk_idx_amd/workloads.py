@@ -34,6 +34,7 @@ LAYOUT_MASKED = 1
 QUANT_NONE = 0
 QUANT_FP8_F32 = 1
 QUANT_FP8_UE8M0 = 2
+QUANT_MXFP8 = 3
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,8 +71,8 @@ class Workload:
         return self.E * self.capacity
 
 
-# The five workloads, named by what they are.  The third field of each name
-# is the token count.
+# The workloads, named by what they are; the field starting with T is the
+# token count.
 WORKLOADS = {
     "tiny_T64": Workload(
         "tiny_T64", T=64, H=256, E=8, K=2, R=2, layout=LAYOUT_CONTIGUOUS,
@@ -88,6 +89,11 @@ WORKLOADS = {
     "deepseekv3_prefill_T8192": Workload(
         "deepseekv3_prefill_T8192", T=8192, H=7168, E=256, K=8, R=8,
         layout=LAYOUT_CONTIGUOUS, align=128, quant=QUANT_FP8_UE8M0,
+        routing="group", seed=4, outlier_frac=0.01),
+    # The DeepSeek-V3 prefill batch (same seed, same inputs) dispatched as 1x32 MXFP8.
+    "deepseekv3_prefill_T8192_mxfp8": Workload(
+        "deepseekv3_prefill_T8192_mxfp8", T=8192, H=7168, E=256, K=8, R=8,
+        layout=LAYOUT_CONTIGUOUS, align=128, quant=QUANT_MXFP8,
         routing="group", seed=4, outlier_frac=0.01),
     # Skewed prefill: four variants of one input set (same seed).
     "skewed_prefill_T16384_contig_bf16": Workload(

@@ -66,7 +66,9 @@ typedef enum {
 typedef enum {
     MOE_QUANT_NONE = 0,      /* bf16 rows, bit copies of the input */
     MOE_QUANT_FP8_F32 = 1,   /* E4M3 rows + fp32 scale per 128 channels */
-    MOE_QUANT_FP8_UE8M0 = 2  /* E4M3 rows + one exponent byte per 128 channels, 4 per uint32 */
+    MOE_QUANT_FP8_UE8M0 = 2, /* E4M3 rows + one exponent byte per 128 channels, 4 per uint32 */
+    MOE_QUANT_MXFP8 = 3      /* E4M3 rows + one E8M0 byte per 32 channels (OCP MX, 1x32 MXFP8
+                                experts with dynamic activation scaling: [A2A] format check) */
 } moe_quant_t;
 
 /* Problem shape, fixed for the lifetime of the buffers sized from it.
@@ -77,7 +79,7 @@ typedef enum {
  * overrides it is a known pitfall ([V2-PR] Modifications, sizing item). */
 typedef struct {
     int32_t max_tokens;  /* per-call token cap (>= 0); num_tokens > max_tokens -> MOE_ERR_CAPACITY */
-    int32_t hidden;      /* H: channels per token, multiple of 8 (of 128 with FP8) */
+    int32_t hidden;      /* H: channels per token, multiple of 8 (of 128 with any FP8 format) */
     int32_t num_experts; /* E: routed experts, 1..2048 */
     int32_t num_topk;    /* K: experts per token, 1..32 ([V2-PR] top-k thread: kNumTopk <= 32) */
     int32_t num_ranks;   /* R: virtual destination ranks, E % R == 0; rank r owns experts [r*E/R, (r+1)*E/R) */
@@ -155,14 +157,19 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens,
  *   out_scale       quant FP8_F32: fp32 [rows_capacity, H/128];
  *                   quant FP8_UE8M0: uint32 [rows_capacity, ceil(H/512)], byte
  *                   b%4 of word b/4 = k_b + 127 where 2^k_b is block b's scale,
- *                   unused high bytes 0; must be NULL for quant NONE.
+ *                   unused high bytes 0;
+ *                   quant MXFP8: uint8 [rows_capacity, H/32], byte b = s_b + 127
+ *                   (E8M0) where 2^s_b is 32-channel block b's scale;
+ *                   must be NULL for quant NONE.
  *   out_row_weight  optional fp32 [rows_capacity]: router weight of the pair in
  *                   each written row (recv_topk_weights); NULL to skip.
  *
  * Per token t and 128-channel block b: amax = max|x|, a = max(amax, 1e-10);
  * fp32 scales: s = a/448 and q = E4M3(clamp(x/s, -448, 448)); UE8M0: k =
- * smallest integer with a <= 448*2^k and q = E4M3(x*2^-k).  E4M3 is the OCP
- * format (max 448), round to nearest even, sign kept.  Each token is read and
+ * smallest integer with a <= 448*2^k and q = E4M3(x*2^-k).  MXFP8 (OCP MX
+ * conversion, per 32-channel block): s = floor(log2 a) - 8 and
+ * q = E4M3(clamp(x*2^-s, -448, 448)), so values above 448*2^s saturate.  E4M3 is
+ * the OCP format (max 448), round to nearest even, sign kept.  Each token is read and
  * quantized once and its bytes stored to all of its kept rows.  Rows that no
  * kept pair maps to (padding, empty masked slots, dropped pairs) are NOT
  * written, in out_x, out_scale and out_row_weight alike.

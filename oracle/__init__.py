@@ -26,6 +26,7 @@ MASKED = 1
 QUANT_NONE = 0
 QUANT_FP8_F32 = 1
 QUANT_FP8_UE8M0 = 2
+QUANT_MXFP8 = 3
 
 _lib = None
 
@@ -67,7 +68,7 @@ def _load():
     lib.oracle_combine_reduce.argtypes = [i32, i32, i32, P, P, P]
     lib.oracle_combine_reduce.restype = None
     for name in ("oracle_bf16_rne_array", "oracle_e4m3_encode_array",
-                 "oracle_ue8m0_exponent_array"):
+                 "oracle_ue8m0_exponent_array", "oracle_mx_exponent_array"):
         getattr(lib, name).argtypes = [P, P, i64]
         getattr(lib, name).restype = None
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
@@ -133,6 +134,8 @@ def dispatch(x: np.ndarray, pair_to_row: np.ndarray, K: int, quant: int, rows: i
         out_scale = np.zeros((rows, NB), np.float32)
     if out_scale is None and quant == QUANT_FP8_UE8M0:
         out_scale = np.zeros((rows, (NB + 3) // 4), np.uint32)
+    if out_scale is None and quant == QUANT_MXFP8:
+        out_scale = np.zeros((rows, H // 32), np.uint8)
     w = None if topk_w is None else _c(topk_w, np.float32)
     for a in (out_x, out_scale, out_row_weight):
         assert a is None or a.flags["C_CONTIGUOUS"]
@@ -161,6 +164,8 @@ def _dispatched_buffers(rows, H, quant, out_x, out_scale):
         out_scale = np.zeros((rows, NB), np.float32)
     if out_scale is None and quant == QUANT_FP8_UE8M0:
         out_scale = np.zeros((rows, (NB + 3) // 4), np.uint32)
+    if out_scale is None and quant == QUANT_MXFP8:
+        out_scale = np.zeros((rows, H // 32), np.uint8)
     for a in (out_x, out_scale):
         assert a is None or a.flags["C_CONTIGUOUS"]
     return out_x, out_scale
@@ -275,4 +280,13 @@ def ue8m0_exponent(a: np.ndarray) -> np.ndarray:
     a = _c(a, np.float32)
     out = np.empty(a.shape, np.int32)
     lib.oracle_ue8m0_exponent_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def mx_exponent(a: np.ndarray) -> np.ndarray:
+    """OCP MX shared exponent for E4M3 elements: largest s with 2^(s+8) <= a."""
+    lib = _load()
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.int32)
+    lib.oracle_mx_exponent_array(_ptr(a), _ptr(out), a.size)
     return out

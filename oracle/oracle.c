@@ -179,6 +179,23 @@ int oracle_ue8m0_exponent(float a)
     return k;
 }
 
+/* OCP MX shared exponent for E4M3 elements (OCP Microscaling Formats
+ * specification, conversion to MX: the shared exponent is floor(log2(a))
+ * minus the largest exponent of the element format, which is 8 for E4M3
+ * since 448 = 1.75 * 2^8): the largest integer s with 2^(s+8) <= a.
+ * Evaluated exactly in double by search. */
+int oracle_mx_exponent(float a)
+{
+    double ad = (double)a;
+    assert(ad > 0.0 && isfinite(ad));
+    int s = 0;
+    while (ldexp(1.0, s + 8) > ad)
+        s--;
+    while (ldexp(1.0, s + 9) <= ad)
+        s++;
+    return s;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Layout: counts, offsets, stable slots, source-index maps                 */
 /* ------------------------------------------------------------------------ */
@@ -280,10 +297,11 @@ int oracle_dispatch_layout(int32_t T, int32_t K, int32_t E, int32_t R,
 /* Dispatch: row permutation, optional fused FP8 1x128 quantization          */
 /* ------------------------------------------------------------------------ */
 
-enum { ORACLE_QUANT_NONE = 0, ORACLE_QUANT_FP8_F32 = 1, ORACLE_QUANT_FP8_UE8M0 = 2 };
+enum { ORACLE_QUANT_NONE = 0, ORACLE_QUANT_FP8_F32 = 1, ORACLE_QUANT_FP8_UE8M0 = 2, ORACLE_QUANT_MXFP8 = 3 };
 
 #define ORACLE_BLOCK 128          /* activation quantization group, 1 x 128 */
 #define ORACLE_AMAX_FLOOR 1e-10f  /* keeps the scale of an all-zero block finite */
+#define ORACLE_MX_BLOCK 32        /* MXFP8 group, 1 x 32 */
 
 /* Quantize one token row (H channels) into E4M3 bytes `q` and its per-block
  * scales.  For block b (channels 128b .. 128b+127):
@@ -296,6 +314,38 @@ enum { ORACLE_QUANT_NONE = 0, ORACLE_QUANT_FP8_F32 = 1, ORACLE_QUANT_FP8_UE8M0 =
 static void quantize_token_row(int32_t H, int32_t quant, const uint16_t *x,
                                uint8_t *q, float *s32, uint32_t *w32)
 {
+    if (quant == ORACLE_QUANT_MXFP8) {
+        /* MXFP8 (1x32, OCP MX): per block of 32 channels, amax and the floor a
+         * as above, shared exponent s = oracle_mx_exponent(a), scale byte
+         * s + 127 (E8M0, byte b of the row's scale bytes, passed in w32),
+         * q = E4M3(clamp(x * 2^-s, +-448)); the clamp binds when a * 2^-s
+         * exceeds 448 (it lies in [256, 512)). */
+        uint8_t *e8 = (uint8_t *)w32;
+        for (int32_t b = 0; b < H / ORACLE_MX_BLOCK; b++) {
+            const uint16_t *xb = x + (int64_t)b * ORACLE_MX_BLOCK;
+            float amax = 0.0f;
+            for (int j = 0; j < ORACLE_MX_BLOCK; j++) {
+                float v = fabsf(oracle_bf16_to_float(xb[j]));
+                assert(isfinite(v));
+                if (v > amax)
+                    amax = v;
+            }
+            float a = amax > ORACLE_AMAX_FLOOR ? amax : ORACLE_AMAX_FLOOR;
+            int sx = oracle_mx_exponent(a);
+            assert(sx + 127 >= 1 && sx + 127 <= 254);
+            e8[b] = (uint8_t)(sx + 127);
+            for (int j = 0; j < ORACLE_MX_BLOCK; j++) {
+                float v = ldexpf(oracle_bf16_to_float(xb[j]), -sx);
+                if (v > 448.0f)
+                    v = 448.0f;
+                if (v < -448.0f)
+                    v = -448.0f;
+                q[(int64_t)b * ORACLE_MX_BLOCK + j] = oracle_e4m3_encode(v);
+            }
+        }
+        (void)s32;
+        return;
+    }
     int32_t NB = H / ORACLE_BLOCK;
     if (quant == ORACLE_QUANT_FP8_UE8M0)
         for (int32_t w = 0; w < (NB + 3) / 4; w++)
@@ -337,8 +387,9 @@ static void quantize_token_row(int32_t H, int32_t quant, const uint16_t *x,
  * For every kept pair p (pair_to_row[p] >= 0) of token t = p / K:
  *   quant NONE : out_x[row, :] = x[t, :]           (bf16 bit copy, H*2 bytes)
  *   quant FP8  : out_x[row, :] = E4M3 bytes of x[t, :] (H bytes) and the
- *                row's scales in out_scale (fp32 [rows, H/128] or packed
- *                UE8M0 uint32 [rows, ceil(H/512)]).
+ *                row's scales in out_scale (fp32 [rows, H/128], packed
+ *                UE8M0 uint32 [rows, ceil(H/512)], or MXFP8 E8M0 bytes
+ *                uint8 [rows, H/32]).
  *   out_row_weight[row] = topk_w[p] when both pointers are given.
  * Quantization happens once per token; every kept row of the token receives
  * the same bytes.  Rows that no kept pair maps to are not written.
@@ -356,7 +407,8 @@ void oracle_dispatch(int32_t T, int32_t K, int32_t H, int32_t quant,
     if (quant != ORACLE_QUANT_NONE) {
         q = (uint8_t *)malloc((size_t)H);
         s32 = (float *)malloc(sizeof(float) * (size_t)(NB > 0 ? NB : 1));
-        w32 = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(NW > 0 ? NW : 1));
+        /* packed UE8M0 words, or the MX scale bytes (H/32 <= 4 * NW words) */
+        w32 = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(4 * NW > 0 ? 4 * NW : 1));
         assert(q && s32 && w32);
     }
     for (int32_t t = 0; t < T; t++) {
@@ -385,6 +437,10 @@ void oracle_dispatch(int32_t T, int32_t K, int32_t H, int32_t quant,
                     float *sd = (float *)out_scale + (int64_t)row * NB;
                     for (int32_t b = 0; b < NB; b++)
                         sd[b] = s32[b];
+                } else if (quant == ORACLE_QUANT_MXFP8) {
+                    int32_t NX = H / ORACLE_MX_BLOCK;
+                    uint8_t *sd = (uint8_t *)out_scale + (int64_t)row * NX;
+                    memcpy(sd, w32, (size_t)NX);
                 } else {
                     uint32_t *wd = (uint32_t *)out_scale + (int64_t)row * NW;
                     for (int32_t w = 0; w < NW; w++)
@@ -509,6 +565,8 @@ static int64_t scale_bytes(int32_t H, int32_t quant)
         return 4 * (int64_t)NB;
     if (quant == ORACLE_QUANT_FP8_UE8M0)
         return 4 * (int64_t)((NB + 3) / 4);
+    if (quant == ORACLE_QUANT_MXFP8)
+        return (int64_t)(H / ORACLE_MX_BLOCK);
     return 0;
 }
 
@@ -630,6 +688,12 @@ void oracle_e4m3_encode_array(const float *in, uint8_t *out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++)
         out[i] = oracle_e4m3_encode(in[i]);
+}
+
+void oracle_mx_exponent_array(const float *in, int32_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_mx_exponent(in[i]);
 }
 
 void oracle_ue8m0_exponent_array(const float *in, int32_t *out, int64_t n)

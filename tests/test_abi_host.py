@@ -98,7 +98,9 @@ def test_size_queries(lib):
     (dict(layout=M.LAYOUT_MASKED, capacity=0, align=0), M.MOE_ERR_INVALID_ARG),
     (dict(layout=M.LAYOUT_MASKED, capacity=5, align=0), M.MOE_OK),  # align unused
     (dict(layout=2), M.MOE_ERR_INVALID_ARG),
-    (dict(quant=3), M.MOE_ERR_INVALID_ARG),
+    (dict(quant=4), M.MOE_ERR_INVALID_ARG),
+    (dict(quant=M.QUANT_MXFP8), M.MOE_OK),
+    (dict(hidden=264, quant=M.QUANT_MXFP8), M.MOE_ERR_INVALID_ARG),       # MX needs H % 128 too
     (dict(num_cus=-1), M.MOE_ERR_INVALID_ARG),
     (dict(max_tokens=-1), M.MOE_ERR_INVALID_ARG),
     (dict(num_experts=4096, num_ranks=1), M.MOE_ERR_UNSUPPORTED),

@@ -23,7 +23,7 @@ import torch
 import combine_topk_idx_amd as M
 import oracle
 from combine_topk_idx_amd import workloads as W
-from test_gpu_parity import SENT, Guarded, _sentinel, make_cfg, scale_cols
+from test_gpu_parity import SENT, Guarded, _sentinel, make_cfg, oracle_scale_view, scale_cols, scale_guard
 
 pytestmark = pytest.mark.gpu
 
@@ -40,11 +40,7 @@ def _say(msg):
 
 
 def _scale_view(quant, buf, rows):
-    if quant == W.QUANT_FP8_F32:
-        return buf.view(np.float32).reshape(rows, -1)
-    if quant == W.QUANT_FP8_UE8M0:
-        return buf.view(np.uint32).reshape(rows, -1)
-    return None
+    return oracle_scale_view(quant, buf, rows)
 
 
 def run_gpu(wl, idx, x, w, y, cfg):
@@ -65,11 +61,11 @@ def run_gpu(wl, idx, x, w, y, cfg):
     h = M.Handle(cfg)
     ws = torch.empty(M.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     send_x = Guarded(qrows * H * eb, torch.uint8 if fp8 else torch.int16, (qrows, H))
-    send_sc = Guarded(qrows * nsc * 4, torch.int32, (qrows, nsc)) if fp8 else None
+    send_sc = scale_guard(wl, qrows) if fp8 else None
     exp_x = Guarded(rows * H * eb, torch.uint8 if fp8 else torch.int16, (rows, H))
-    exp_sc = Guarded(rows * nsc * 4, torch.int32, (rows, nsc)) if fp8 else None
+    exp_sc = scale_guard(wl, rows) if fp8 else None
     dir_x = Guarded(rows * H * eb, torch.uint8 if fp8 else torch.int16, (rows, H))
-    dir_sc = Guarded(rows * nsc * 4, torch.int32, (rows, nsc)) if fp8 else None
+    dir_sc = scale_guard(wl, rows) if fp8 else None
     partial = Guarded(qrows * H * 2, torch.int16, (qrows, H))
     out = Guarded(T * H * 2, torch.int16, (T, H))
     d_idx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
@@ -208,6 +204,7 @@ SMALL = [
     ("K32_R8", "tiny_T64", dict(T=50, E=64, R=8, K=32, H=256, quant=W.QUANT_FP8_F32)),
     ("masked_drops_ue8m0", "deepseekv3_decode_T256", dict(T=300, H=512, capacity=3,
                                                           quant=W.QUANT_FP8_UE8M0)),
+    ("mxfp8_contig", "deepseekv3_prefill_T8192", dict(T=500, H=1024, quant=W.QUANT_MXFP8)),
     ("many_chunks_T140000", "tiny_T64", dict(T=140000, E=64, R=16, K=2, H=64)),
     ("lds_budget_T1100000_R32", "tiny_T64", dict(T=1100000, E=32, R=32, K=1, H=8)),
 ]

@@ -28,6 +28,8 @@ CASES = {
     "deepseekv3_decode_T256": W.WORKLOADS["deepseekv3_decode_T256"],
     "contig_ue8m0_T300_H1024": W.WORKLOADS["deepseekv3_prefill_T8192"].replace(
         name="contig_ue8m0_T300_H1024", T=300, H=1024),
+    "contig_mxfp8_T200_H512": W.WORKLOADS["deepseekv3_prefill_T8192"].replace(
+        name="contig_mxfp8_T200_H512", T=200, H=512, quant=W.QUANT_MXFP8),
     "contig_bf16_T64_H256": W.WORKLOADS["tiny_T64"].replace(
         name="contig_bf16_T64_H256", expert_output="random"),
     # beyond the one-launch limit (T*K > 65536): the fused call runs two kernels
@@ -109,6 +111,8 @@ def _check_oracle(wl, inp, y, got, rows):
         sv = osc.view(np.float32).reshape(rows, -1)
     elif wl.quant == W.QUANT_FP8_UE8M0:
         sv = osc.view(np.uint32).reshape(rows, -1)
+    elif wl.quant == W.QUANT_MXFP8:
+        sv = osc.view(np.uint8).reshape(rows, -1)
     oracle.dispatch(inp.x, h["pair_to_row"], wl.K, wl.quant, rows, topk_w=inp.topk_w,
                     out_x=ox.view(np.uint8 if fp8 else np.uint16).reshape(rows, wl.H),
                     out_scale=sv, out_row_weight=orw.view(np.float32))

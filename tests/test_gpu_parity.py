@@ -65,8 +65,29 @@ def make_cfg(wl, T_max=None, num_cus=0):
 
 
 def scale_cols(wl):
+    """32-bit words of scales per dispatched row."""
     nb = wl.H // 128
-    return {W.QUANT_NONE: 0, W.QUANT_FP8_F32: nb, W.QUANT_FP8_UE8M0: (nb + 3) // 4}[wl.quant]
+    return {W.QUANT_NONE: 0, W.QUANT_FP8_F32: nb, W.QUANT_FP8_UE8M0: (nb + 3) // 4,
+            W.QUANT_MXFP8: nb}[wl.quant]
+
+
+def scale_guard(wl, rows):
+    """A guarded device scale buffer in the element type the binding expects."""
+    if wl.quant == W.QUANT_MXFP8:
+        return Guarded(rows * wl.H // 32, torch.uint8, (rows, wl.H // 32))
+    nsc = scale_cols(wl)
+    return Guarded(rows * nsc * 4, torch.int32, (rows, nsc))
+
+
+def oracle_scale_view(quant, buf, rows):
+    """The oracle's view of a scale buffer: fp32, packed UE8M0 words or MX bytes."""
+    if quant == W.QUANT_FP8_F32:
+        return buf.view(np.float32).reshape(rows, -1)
+    if quant == W.QUANT_FP8_UE8M0:
+        return buf.view(np.uint32).reshape(rows, -1)
+    if quant == W.QUANT_MXFP8:
+        return buf.view(np.uint8).reshape(rows, -1)
+    return None
 
 
 def run_gpu(wl, idx, w, x, y, cfg, fused=False):
@@ -88,7 +109,7 @@ def run_gpu(wl, idx, w, x, y, cfg, fused=False):
     ebytes = 1 if fp8 else 2
     out_x = Guarded(rows * H * ebytes, torch.uint8 if fp8 else torch.int16, (rows, H))
     nsc = scale_cols(wl)
-    out_scale = Guarded(rows * nsc * 4, torch.int32, (rows, nsc)) if fp8 else None
+    out_scale = scale_guard(wl, rows) if fp8 else None
     out_rw = Guarded(rows * 4, torch.float32, (rows,))
     out = Guarded(T * H * 2, torch.int16, (T, H))
     d_idx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
@@ -129,11 +150,7 @@ def run_oracle(wl, idx, w, x, y, cfg):
     osc = _sentinel(rows * nsc * 4) if fp8 else None
     orw = _sentinel(rows * 4)
     out_x = ox.view(np.uint8 if fp8 else np.uint16).reshape(rows, H)
-    out_scale = None
-    if wl.quant == W.QUANT_FP8_F32:
-        out_scale = osc.view(np.float32).reshape(rows, nsc)
-    elif wl.quant == W.QUANT_FP8_UE8M0:
-        out_scale = osc.view(np.uint32).reshape(rows, nsc)
+    out_scale = oracle_scale_view(wl.quant, osc, rows) if fp8 else None
     oracle.dispatch(x, h["pair_to_row"], K, wl.quant, rows, topk_w=w, out_x=out_x,
                     out_scale=out_scale, out_row_weight=orw.view(np.float32))
     res["out_x"] = ox
@@ -224,6 +241,9 @@ SMALL = [
     # T, H, E, K, R, layout, align, capacity, quant
     (37, 384, 24, 6, 4, W.LAYOUT_CONTIGUOUS, 16, 1, W.QUANT_FP8_UE8M0),
     (37, 384, 24, 6, 4, W.LAYOUT_CONTIGUOUS, 16, 1, W.QUANT_FP8_F32),
+    (37, 384, 24, 6, 4, W.LAYOUT_CONTIGUOUS, 16, 1, W.QUANT_MXFP8),
+    (300, 640, 40, 7, 8, W.LAYOUT_MASKED, 1, 33, W.QUANT_MXFP8),         # MX, overflow
+    (2000, 128, 96, 32, 8, W.LAYOUT_CONTIGUOUS, 8, 1, W.QUANT_MXFP8),    # MX, K = 32, one group
     (300, 640, 40, 7, 8, W.LAYOUT_CONTIGUOUS, 3, 1, W.QUANT_FP8_UE8M0),   # 5 blocks: partial word
     (300, 1152, 40, 7, 5, W.LAYOUT_MASKED, 1, 33, W.QUANT_FP8_F32),       # overflow
     (513, 72, 17, 3, 17, W.LAYOUT_CONTIGUOUS, 5, 1, W.QUANT_NONE),        # H % 512 ragged
@@ -280,6 +300,7 @@ def _edge_inputs(kind, T, H, E, K, rng):
 @pytest.mark.parametrize("kind", ["one_expert", "invalid_and_unrouted", "duplicates"])
 @pytest.mark.parametrize("layout,quant", [(W.LAYOUT_CONTIGUOUS, W.QUANT_FP8_UE8M0),
                                           (W.LAYOUT_MASKED, W.QUANT_FP8_F32),
+                                          (W.LAYOUT_MASKED, W.QUANT_MXFP8),
                                           (W.LAYOUT_MASKED, W.QUANT_NONE)])
 def test_edge_routing(kind, layout, quant, fused):
     T, H, E, K, R = 200, 256, 12, 4, 3
@@ -375,7 +396,7 @@ def test_quant_sweep_all_bf16_magnitudes():
     xf[:allb.size] = allb
     x = W.f32_to_bf16_bits(xf.reshape(T, H))
     rng = np.random.default_rng(77)
-    for quant in (W.QUANT_FP8_UE8M0, W.QUANT_FP8_F32):
+    for quant in (W.QUANT_FP8_UE8M0, W.QUANT_FP8_F32, W.QUANT_MXFP8):
         _say(f"bf16 magnitude sweep quant {quant} T={T}")
         wl = W.Workload("sweep", T=T, H=H, E=4, K=2, R=2, layout=W.LAYOUT_CONTIGUOUS,
                         align=1, quant=quant)

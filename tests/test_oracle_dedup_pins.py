@@ -155,12 +155,15 @@ def _sentinel_bufs(rows, H, quant):
         sc = np.full((rows, NB * 4), SENT, np.uint8).view(np.float32)
     elif quant == oracle.QUANT_FP8_UE8M0:
         sc = np.full((rows, (NB + 3) // 4 * 4), SENT, np.uint8).view(np.uint32)
+    elif quant == oracle.QUANT_MXFP8:
+        sc = np.full((rows, H // 32), SENT, np.uint8)
     else:
         sc = None
     return ox, sc
 
 
-@pytest.mark.parametrize("quant", [oracle.QUANT_NONE, oracle.QUANT_FP8_F32, oracle.QUANT_FP8_UE8M0])
+@pytest.mark.parametrize("quant", [oracle.QUANT_NONE, oracle.QUANT_FP8_F32, oracle.QUANT_FP8_UE8M0,
+                                   oracle.QUANT_MXFP8])
 @pytest.mark.parametrize("layout", [oracle.CONTIGUOUS, oracle.MASKED])
 def test_expand_of_dedup_equals_direct_dispatch(oracle_lib, quant, layout):
     """Sending each token once per rank and expanding on the receiver gives
