@@ -67,6 +67,14 @@ def _load():
     lib.oracle_combine_partial.restype = None
     lib.oracle_combine_reduce.argtypes = [i32, i32, i32, P, P, P]
     lib.oracle_combine_reduce.restype = None
+    lib.oracle_row_expert.argtypes = [i32, P, P, i64, P]
+    lib.oracle_row_expert.restype = None
+    lib.oracle_repack_masked_to_contiguous.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, P]
+    lib.oracle_repack_masked_to_contiguous.restype = ctypes.c_int
+    lib.oracle_repack_contiguous_to_masked.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_repack_contiguous_to_masked.restype = None
+    lib.oracle_scales_mn_major.argtypes = [i64, i32, P, P]
+    lib.oracle_scales_mn_major.restype = None
     for name in ("oracle_bf16_rne_array", "oracle_e4m3_encode_array",
                  "oracle_ue8m0_exponent_array", "oracle_mx_exponent_array"):
         getattr(lib, name).argtypes = [P, P, i64]
@@ -289,4 +297,62 @@ def mx_exponent(a: np.ndarray) -> np.ndarray:
     a = _c(a, np.float32)
     out = np.empty(a.shape, np.int32)
     lib.oracle_mx_exponent_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+# ---- adapters for grouped-GEMM consumers --------------------------------------
+
+def row_expert(expert_offset: np.ndarray, recv_count: np.ndarray, rows: int) -> np.ndarray:
+    """Expert of each row that holds a received pair, -1 elsewhere: int32 [rows]."""
+    lib = _load()
+    off, rc = _c(expert_offset, np.int32), _c(recv_count, np.int32)
+    out = np.zeros(rows, np.int32)
+    lib.oracle_row_expert(rc.size, _ptr(off), _ptr(rc), rows, _ptr(out))
+    return out
+
+
+def repack_masked_to_contiguous(x: np.ndarray, scale: Optional[np.ndarray], recv_count: np.ndarray,
+                                C: int, align: int, quant: int, out_rows: int,
+                                out_x: Optional[np.ndarray] = None, out_scale: Optional[np.ndarray] = None):
+    """Masked slab rows (+ scales) -> contiguous segments padded to `align`.
+    Returns (out_x, out_scale, out_offset [E+1], out_row_expert [out_rows])."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    H = x.shape[1]
+    rc = _c(recv_count, np.int32)
+    E = rc.size
+    out_x, out_scale = _dispatched_buffers(out_rows, H, quant, out_x, out_scale)
+    off = np.zeros(E + 1, np.int32)
+    rex = np.zeros(out_rows, np.int32)
+    sc = None if scale is None else np.ascontiguousarray(scale)
+    rc_ = lib.oracle_repack_masked_to_contiguous(E, C, align, H, quant, _ptr(rc), _ptr(x), _ptr(sc), out_rows,
+                                                 _ptr(out_x), _ptr(out_scale), _ptr(off), _ptr(rex))
+    if rc_ != 0:
+        raise ValueError("contiguous segments exceed out_rows")
+    return out_x, out_scale, off, rex
+
+
+def repack_contiguous_to_masked(y: np.ndarray, recv_count: np.ndarray, offset: np.ndarray, C: int,
+                                out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Contiguous bf16 expert outputs -> the masked slab [E*C, H]."""
+    lib = _load()
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    rc = _c(recv_count, np.int32)
+    E = rc.size
+    if out is None:
+        out = np.zeros((E * C, H), np.uint16)
+    assert out.flags["C_CONTIGUOUS"]
+    lib.oracle_repack_contiguous_to_masked(E, C, H, _ptr(rc), _ptr(_c(offset, np.int32)), _ptr(y), _ptr(out))
+    return out
+
+
+def scales_mn_major(scale_words: np.ndarray) -> np.ndarray:
+    """Row-major 32-bit scales [rows, S] -> MN-major [S, ld], ld = rows rounded up to 4."""
+    lib = _load()
+    a = np.ascontiguousarray(scale_words).view(np.uint32)
+    rows, S = a.shape
+    ld = (rows + 3) // 4 * 4
+    out = np.zeros((S, ld), np.uint32)
+    lib.oracle_scales_mn_major(rows, S, _ptr(a), _ptr(out))
     return out

@@ -40,6 +40,13 @@
  *     rank, expanded to per-expert rows on the receiver, and combined as
  *     per-rank partial sums reduced again on the source (the multiple-
  *     reduction option on page vLLM tools/ep_kernels, commit message).
+ *   - MXFP8 dispatch for 1x32 MXFP8 experts with dynamic activation scaling
+ *     (page "[Feature] Add DeepEPv2 (ElasticBuffer) MoE A2A backend", format
+ *     check), following the OCP Microscaling conversion.
+ *   - Adapters for grouped-GEMM consumers: per-row expert indices, masked <->
+ *     contiguous repack and MN-major scales (same page, Implementation:
+ *     masked-slab repack kernels and GEMM adapters with fp32 and packed UE8M0
+ *     scales).
  *
  * The pages leave row order, alignment, overflow handling, scale formulas and
  * rounding open; the readings taken here are listed in the design doc and in the
@@ -672,6 +679,87 @@ void oracle_combine_reduce(int32_t T, int32_t R, int32_t H, const uint16_t *part
             out[(int64_t)t * H + j] = oracle_bf16_rne(acc);
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Adapters for grouped-GEMM consumers: per-row experts, masked <-> contiguous */
+/* repack, MN-major scales                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages add masked-slab repack kernels and grouped-GEMM adapters for
+ * contiguous prefill and masked decode, with fp32 and packed UE8M0 scales
+ * (page "[Feature] Add DeepEPv2 (ElasticBuffer) MoE A2A backend",
+ * Implementation).  Readings taken here: a contiguous grouped GEMM reads one
+ * expert index per row (-1 for rows it must skip); a masked slab is repacked
+ * by moving expert e's first recv_count[e] rows back to back, each segment
+ * padded to `align` rows, and expert outputs come back the same way; scales
+ * are read in MN-major order (scale j of row r at j*ld + r) with the leading
+ * dimension rounded up to 16 bytes.
+ */
+
+/* row_expert[r] = e for every row r that holds one of expert e's received
+ * pairs (rows off[e] .. off[e] + recv_count[e] - 1, where off[e] =
+ * expert_offset[e]), -1 for every other row in [0, rows). */
+void oracle_row_expert(int32_t E, const int32_t *expert_offset, const int32_t *recv_count,
+                       int64_t rows, int32_t *row_expert)
+{
+    for (int64_t r = 0; r < rows; r++)
+        row_expert[r] = -1;
+    for (int32_t e = 0; e < E; e++)
+        for (int32_t s = 0; s < recv_count[e]; s++)
+            row_expert[(int64_t)expert_offset[e] + s] = e;
+}
+
+/* Masked slab -> contiguous segments: out_offset[0] = 0, out_offset[e+1] =
+ * out_offset[e] + recv_count[e] rounded up to `align`; row s < recv_count[e]
+ * of expert e moves from e*C + s to out_offset[e] + s, with its scales.
+ * Padding rows are not written; out_row_expert covers [0, out_rows).
+ * Returns -1 if the segments exceed out_rows. */
+int oracle_repack_masked_to_contiguous(int32_t E, int32_t C, int32_t align, int32_t H, int32_t quant,
+                                       const int32_t *recv_count, const void *x, const void *scale,
+                                       int64_t out_rows, void *out_x, void *out_scale,
+                                       int32_t *out_offset, int32_t *out_row_expert)
+{
+    int64_t rb = row_bytes(H, quant), sb = scale_bytes(H, quant);
+    out_offset[0] = 0;
+    for (int32_t e = 0; e < E; e++)
+        out_offset[e + 1] = out_offset[e] + (recv_count[e] + align - 1) / align * align;
+    if ((int64_t)out_offset[E] > out_rows)
+        return -1;
+    for (int32_t e = 0; e < E; e++) {
+        for (int32_t s = 0; s < recv_count[e]; s++) {
+            int64_t src = (int64_t)e * C + s, dst = (int64_t)out_offset[e] + s;
+            memcpy((uint8_t *)out_x + dst * rb, (const uint8_t *)x + src * rb, (size_t)rb);
+            if (sb > 0)
+                memcpy((uint8_t *)out_scale + dst * sb, (const uint8_t *)scale + src * sb, (size_t)sb);
+        }
+    }
+    oracle_row_expert(E, out_offset, recv_count, out_rows, out_row_expert);
+    return 0;
+}
+
+/* Contiguous expert outputs -> masked slab: y_masked[e*C + s] = y[offset[e] + s]
+ * for s < recv_count[e] (bf16 rows of H channels); other slab rows are not
+ * written.  `offset` is the out_offset of the masked-to-contiguous repack. */
+void oracle_repack_contiguous_to_masked(int32_t E, int32_t C, int32_t H, const int32_t *recv_count,
+                                        const int32_t *offset, const uint16_t *y, uint16_t *y_masked)
+{
+    for (int32_t e = 0; e < E; e++)
+        for (int32_t s = 0; s < recv_count[e]; s++)
+            memcpy(y_masked + ((int64_t)e * C + s) * H, y + ((int64_t)offset[e] + s) * H,
+                   sizeof(uint16_t) * (size_t)H);
+}
+
+/* Row-major 32-bit scales [rows, S] -> MN-major [S, ld]: out[j*ld + r] =
+ * in[r*S + j] for r < rows and 0 for rows <= r < ld, ld = rows rounded up to a
+ * multiple of 4 (16 bytes). */
+void oracle_scales_mn_major(int64_t rows, int32_t S, const uint32_t *in, uint32_t *out)
+{
+    int64_t ld = (rows + 3) / 4 * 4;
+    for (int32_t j = 0; j < S; j++)
+        for (int64_t r = 0; r < ld; r++)
+            out[(int64_t)j * ld + r] = r < rows ? in[r * S + j] : 0u;
 }
 
 /* ------------------------------------------------------------------------ */
