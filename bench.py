@@ -85,6 +85,84 @@ def dedup_bytes(wl, n_kept, n_rows):
             "combine_reduce": 4 * T * R + 2 * n_rows * H + 2 * T * H}
 
 
+def row_and_scale_bytes(wl):
+    """(bytes of a dispatched row, bytes of its scales)."""
+    H, nb = wl.H, wl.H // 128
+    return {W.QUANT_NONE: (2 * H, 0), W.QUANT_FP8_F32: (H, 4 * nb),
+            W.QUANT_FP8_UE8M0: (H, 4 * ((nb + 3) // 4)), W.QUANT_MXFP8: (H, H // 32)}[wl.quant]
+
+
+def run_adapters(args, wl, cfg, d_idx, d_w, d_x, bufs, stream):
+    """Times the grouped-GEMM adapters on a masked dispatch: per-row experts,
+    masked -> contiguous repack, contiguous -> masked repack of bf16 expert
+    outputs, MN-major scales; HIP events between the calls."""
+    if wl.layout != W.LAYOUT_MASKED:
+        raise SystemExit("--adapters needs a masked workload")
+    T, H, E, C, A = wl.T, wl.H, wl.E, wl.capacity, args.align
+    dev = d_x.device
+    M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace, stream)
+    M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale, None, stream)
+    crows = M.moe_repack_rows_capacity(cfg, A)
+    rows = bufs.rows
+    out_x = torch.empty((crows, H), dtype=bufs.out_x.dtype, device=dev)
+    out_s = None if bufs.out_scale is None else torch.empty((crows, bufs.out_scale.shape[1]),
+                                                            dtype=bufs.out_scale.dtype, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    rex_c = torch.empty(crows, dtype=torch.int32, device=dev)
+    rex = torch.empty(rows, dtype=torch.int32, device=dev)
+    y_c = torch.randn((crows, H), device=dev).to(torch.bfloat16).view(torch.int16)
+    y_m = torch.empty((rows, H), dtype=torch.int16, device=dev)
+    S = M.moe_scale_words(cfg)
+    ld = (rows + 3) // 4 * 4
+    s_mn = torch.empty(max(S * ld, 1), dtype=torch.int32, device=dev)
+    calls = [
+        ("row_expert", lambda: M.moe_row_expert(cfg, bufs.handle, rex, stream)),
+        ("repack_masked_to_contiguous", lambda: M.moe_repack_masked_to_contiguous(
+            cfg, A, bufs.handle, bufs.out_x, bufs.out_scale, out_x, out_s, off, rex_c, stream)),
+        ("repack_contiguous_to_masked", lambda: M.moe_repack_contiguous_to_masked(
+            cfg, bufs.handle, off, y_c, y_m, stream)),
+    ]
+    if S > 0:
+        calls.append(("scales_mn_major", lambda: M.moe_scales_mn_major(cfg, rows, bufs.out_scale, s_mn, stream)))
+    for _ in range(args.warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(n)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    log(f"[bench] adapters: timing {n} rounds")
+    for i in range(n):
+        for j, (_, f) in enumerate(calls):
+            ev[i][j].record(stream)
+            f()
+        ev[i][-1].record(stream)
+    torch.cuda.synchronize()
+    ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)]))
+          for j, (name, _) in enumerate(calls)}
+    kept = int(bufs.handle.recv_count.cpu().numpy().sum())
+    used = int(off.cpu().numpy()[-1])
+    rb, sb = row_and_scale_bytes(wl)
+    ab = {"row_expert": 4 * rows + 8 * E,
+          "repack_masked_to_contiguous": 2 * kept * (rb + sb) + 4 * crows + 12 * E,
+          "repack_contiguous_to_masked": 2 * kept * 2 * H + 8 * E,
+          "scales_mn_major": 4 * rows * S + 4 * S * ld}
+    ab = {k: v for k, v in ab.items() if k in ms}
+    gbs = {k: ab[k] / (ms[k] * 1e-3) / 1e9 for k in ab}
+    copy_gbs = copy_ceiling(args.calib_copy_mib, dev, stream)
+    return {"metric": "grouped-GEMM adapter GB/s per call (masked dispatch)", "value": gbs["repack_masked_to_contiguous"],
+            "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup, "higher_is_better": True,
+            "vs_baseline": None, "data": "synthetic", "library_sha256": library_hash(),
+            "config": {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "capacity": C, "align": A,
+                       "quant": QUANT_NAME[wl.quant]},
+            "path": {"calls": [c for c, _ in calls], "per_call_ms_mean": ms, "algorithmic_bytes": ab,
+                     "per_call_gbs": gbs, "kept_rows": kept, "contiguous_rows_used": used,
+                     "contiguous_rows_capacity": crows, "copy_ceiling_gbs": copy_gbs}}
+
+
 def copy_ceiling(mib, dev, stream):
     """GB/s of a plain device-to-device copy of `mib` MiB (the attainable
     ceiling next to the kernels; also the counter calibration)."""
@@ -203,16 +281,23 @@ def short_kernel(name):
     -> 'dispatch_rows_fp8_ue8m0'; combine_kernel<false> -> 'combine_kernel',
     combine_kernel<true> -> 'combine_kernel_partial'."""
     base = name.split("(moe::")[0].split("::")[-1]
+    named = {"combine_kernel<false>": "combine_kernel", "combine_kernel<true>": "combine_kernel_partial",
+             "repack_kernel<true>": "repack_to_contiguous", "repack_kernel<false>": "repack_to_masked"}
+    if base in named:
+        return named[base]
     if "<" in base:
         stem, arg = base[:-1].split("<")
-        suffix = {"false": "", "true": "_partial"}.get(arg)
-        base = stem + suffix if suffix is not None else f"{stem}_{QUANT_TEMPLATE.get(arg, arg)}"
+        base = f"{stem}_{QUANT_TEMPLATE.get(arg, arg)}"
     return base
 
 
 def kernel_bytes(bench):
     """Algorithmic bytes per launch of each library kernel a benchmark line ran."""
     ab = bench["path"]["algorithmic_bytes"]
+    if "repack_masked_to_contiguous" in ab:  # grouped-GEMM adapters
+        return {"row_expert_kernel": ab["row_expert"], "repack_to_contiguous": ab["repack_masked_to_contiguous"],
+                "repack_to_masked": ab["repack_contiguous_to_masked"],
+                "scales_mn_major_kernel": ab.get("scales_mn_major")}
     if isinstance(bench["path"]["calls"], list):  # per-rank deduplicated path
         algo = {"rank_layout_kernel": ab["rank_layout"], "layout_single": ab["layout"],
                 "expand_kernel": ab["expand"], "combine_kernel_partial": ab["combine_partial"],
@@ -258,8 +343,9 @@ def summarize(run_dir, calib_mib):
     with open(os.path.join(run_dir, "bench.json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
     wl = W.WORKLOADS[bench["config"]["workload"]]
-    dedup = isinstance(bench["path"]["calls"], list)
-    section = wl.name + (":dedup" if dedup else "")
+    adapters = "repack_masked_to_contiguous" in bench["path"]["algorithmic_bytes"]
+    dedup = isinstance(bench["path"]["calls"], list) and not adapters
+    section = wl.name + (":dedup" if dedup else ":adapters" if adapters else "")
     built = bench.get("library_sha256")
     if built is None:
         raise SystemExit("bench.json names no library_sha256: rerun the benchmark with this build")
@@ -324,8 +410,11 @@ def summarize(run_dir, calib_mib):
         if "moe::" not in name:
             continue
         short = short_kernel(name)
+        if adapters and short not in algo:
+            continue  # the dispatch that sets up the adapters run is profiled on its own
         avg, mn, mx, sd = (float(row[k]) / 1e3 for k in ("AverageNs", "MinNs", "MaxNs", "StdDev"))
-        lines = [f"# {short} -- {wl.name}{' (per-rank deduplicated path)' if dedup else ''} ({title})", "",
+        path_name = " (per-rank deduplicated path)" if dedup else " (grouped-GEMM adapters)" if adapters else ""
+        lines = [f"# {short} -- {wl.name}{path_name} ({title})", "",
                  f"Kernel: `{name}`", "",
                  "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
                  "Command:", "", "    " + trace_cmd, "",
@@ -336,9 +425,11 @@ def summarize(run_dir, calib_mib):
             lines += [f"Algorithmic bytes per launch: {a:,} B -> {a / (avg * 1e3):,.0f} GB/s at the traced "
                       f"average ({a / (avg * 1e3) / HBM_PEAK_GBS:.1%} of the 8 TB/s HBM peak).", ""]
         lines += [f"Benchmark line of the same build (`{bench_cmd}`), HIP events on the launch stream:",
-                  f"step {per_call['event_ms_per_step'] * 1e3:.1f} us, per call "
+                  (f"step {per_call['event_ms_per_step'] * 1e3:.1f} us, " if "event_ms_per_step" in per_call
+                   else "")
+                  + "per call "
                   + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["per_call_ms_mean"].items())
-                  + ("" if dedup else "; separate calls " + ", ".join(
+                  + ("" if "separate_calls_ms_mean" not in per_call else "; separate calls " + ", ".join(
                       f"{k} {v * 1e3:.1f} us" for k, v in per_call["separate_calls_ms_mean"].items()))
                   + ".", ""]
         rec = per_kernel.get(short)
@@ -355,7 +446,7 @@ def summarize(run_dir, calib_mib):
                       f"`{ckey[0]}`, grid {ckey[1]}); per {copy_kib:,.0f} KiB moved its FETCH_SIZE reads "
                       f"{cf:,.1f} KiB and its WRITE_SIZE {cw:,.1f} KiB, so FETCH_SIZE is multiplied by "
                       f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f}.", ""]
-        fname = f"{short}_{wl.name}{'_dedup_path' if dedup else ''}.md"
+        fname = f"{short}_{wl.name}{'_dedup_path' if dedup else '_adapters' if adapters else ''}.md"
         with open(os.path.join(ROOT, "profiles", fname), "w") as f:
             f.write("\n".join(lines))
     print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
@@ -396,6 +487,9 @@ def main():
     ap.add_argument("--dedup", action="store_true",
                     help="time the per-rank deduplicated path instead (rank layout, dedup dispatch, "
                          "expansion, partial combine, reduction)")
+    ap.add_argument("--adapters", action="store_true",
+                    help="time the grouped-GEMM adapters on a masked workload instead")
+    ap.add_argument("--align", type=int, default=128, help="segment alignment for --adapters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -429,6 +523,10 @@ def main():
     d_idx = torch.from_numpy(inp.topk_idx).to(dev)
     d_w = torch.from_numpy(inp.topk_w).to(dev)
     d_x = torch.from_numpy(inp.x.view(np.int16)).to(dev)
+    if args.adapters:  # needs no expert outputs
+        print(json.dumps(run_adapters(args, wl, cfg, d_idx, d_w, d_x, bufs, torch.cuda.current_stream())),
+              flush=True)
+        return
     if wl.expert_output == "random":
         y = W.expert_outputs(wl, inp)
     else:  # outputs that follow the rows' experts: take the row map from the library

@@ -118,6 +118,18 @@ def _load():
     lib.moe_combine_partial.restype = ctypes.c_int
     lib.moe_combine_reduce.argtypes = [cfgp, i32, P, rhp, P, P]
     lib.moe_combine_reduce.restype = ctypes.c_int
+    lib.moe_row_expert.argtypes = [cfgp, hp, P, P]
+    lib.moe_row_expert.restype = ctypes.c_int
+    lib.moe_repack_rows_capacity.argtypes = [cfgp, i32]
+    lib.moe_repack_rows_capacity.restype = sz
+    lib.moe_repack_masked_to_contiguous.argtypes = [cfgp, i32, hp, P, P, P, P, P, P, P]
+    lib.moe_repack_masked_to_contiguous.restype = ctypes.c_int
+    lib.moe_repack_contiguous_to_masked.argtypes = [cfgp, hp, P, P, P, P]
+    lib.moe_repack_contiguous_to_masked.restype = ctypes.c_int
+    lib.moe_scale_words.argtypes = [cfgp]
+    lib.moe_scale_words.restype = sz
+    lib.moe_scales_mn_major.argtypes = [cfgp, i32, P, P, P]
+    lib.moe_scales_mn_major.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -436,3 +448,67 @@ def moe_combine_reduce(cfg: MoeConfig, num_tokens: int, partial: torch.Tensor,
         op = _ptr(out, 2, num_tokens * H, "out")
     _check("moe_combine_reduce", lib.moe_combine_reduce(
         ctypes.byref(cfg), int(num_tokens), pp, ctypes.byref(rank_handle.c), op, _stream(stream)))
+
+
+# ---- adapters for grouped-GEMM consumers --------------------------------------
+
+def moe_repack_rows_capacity(cfg: MoeConfig, align: int) -> int:
+    return int(_load().moe_repack_rows_capacity(ctypes.byref(cfg), int(align)))
+
+
+def moe_scale_words(cfg: MoeConfig) -> int:
+    return int(_load().moe_scale_words(ctypes.byref(cfg)))
+
+
+def moe_row_expert(cfg: MoeConfig, handle: Handle, row_expert: torch.Tensor, stream=None) -> None:
+    """Expert index of every dispatched row (-1 for rows holding no pair)."""
+    lib = _load()
+    rp = _ptr(row_expert, 4, moe_rows_capacity(cfg), "row_expert")
+    _check("moe_row_expert", lib.moe_row_expert(ctypes.byref(cfg), ctypes.byref(handle.c), rp, _stream(stream)))
+
+
+def moe_repack_masked_to_contiguous(cfg: MoeConfig, align: int, handle: Handle, x: torch.Tensor,
+                                    scale: Optional[torch.Tensor], out_x: torch.Tensor,
+                                    out_scale: Optional[torch.Tensor], out_expert_offset: torch.Tensor,
+                                    out_row_expert: torch.Tensor, stream=None) -> None:
+    """Masked slab rows (+ scales) -> contiguous segments padded to `align`."""
+    lib = _load()
+    rows, crows = moe_rows_capacity(cfg), moe_repack_rows_capacity(cfg, align)
+    H = cfg.hidden
+    ob = 2 if cfg.quant == QUANT_NONE else 1
+    xp = _ptr(x, None, rows * H * ob // x.element_size(), "x")
+    sp = _scale_ptr(cfg, scale, rows, "scale")
+    op = _ptr(out_x, None, crows * H * ob // out_x.element_size(), "out_x")
+    osp = _scale_ptr(cfg, out_scale, crows, "out_scale")
+    offp = _ptr(out_expert_offset, 4, cfg.num_experts + 1, "out_expert_offset")
+    rep = _ptr(out_row_expert, 4, crows, "out_row_expert")
+    _check("moe_repack_masked_to_contiguous", lib.moe_repack_masked_to_contiguous(
+        ctypes.byref(cfg), int(align), ctypes.byref(handle.c), xp, sp, op, osp, offp, rep, _stream(stream)))
+
+
+def moe_repack_contiguous_to_masked(cfg: MoeConfig, handle: Handle, expert_offset: torch.Tensor,
+                                    y: torch.Tensor, y_masked: torch.Tensor, stream=None) -> None:
+    """Contiguous bf16 expert outputs -> the masked slab."""
+    lib = _load()
+    rows = moe_rows_capacity(cfg)
+    H = cfg.hidden
+    offp = _ptr(expert_offset, 4, cfg.num_experts + 1, "expert_offset")
+    yp = _ptr(y, 2, 0, "y")
+    mp = _ptr(y_masked, 2, rows * H, "y_masked")
+    _check("moe_repack_contiguous_to_masked", lib.moe_repack_contiguous_to_masked(
+        ctypes.byref(cfg), ctypes.byref(handle.c), offp, yp, mp, _stream(stream)))
+
+
+def moe_scales_mn_major(cfg: MoeConfig, rows: int, scale: torch.Tensor, scale_mn: torch.Tensor,
+                        stream=None) -> None:
+    """Row-major scale words [rows, S] -> MN-major [S, ld], ld = rows rounded up to 4."""
+    lib = _load()
+    S = moe_scale_words(cfg)
+    ld = (int(rows) + 3) // 4 * 4
+    sp = _ptr(scale, None, 0, "scale")
+    if scale.numel() * scale.element_size() < rows * S * 4:
+        raise ValueError("scale: fewer than rows * S words")
+    op = _ptr(scale_mn, None, 0, "scale_mn")
+    if scale_mn.numel() * scale_mn.element_size() < S * ld * 4:
+        raise ValueError("scale_mn: fewer than S * ld words")
+    _check("moe_scales_mn_major", lib.moe_scales_mn_major(ctypes.byref(cfg), int(rows), sp, op, _stream(stream)))

@@ -75,6 +75,28 @@ moe_status_t check_rank_handle(const moe_rank_handle_t *h)
     return MOE_OK;
 }
 
+int32_t scale_words32(const moe_config_t &c)
+{
+    const int32_t NB = c.hidden / kQuantGroup;
+    switch (c.quant) {
+    case MOE_QUANT_FP8_F32:
+        return NB;
+    case MOE_QUANT_FP8_UE8M0:
+        return (NB + 3) / 4;
+    case MOE_QUANT_MXFP8:
+        return NB;  // H/32 E8M0 bytes, four per word
+    default:
+        return 0;
+    }
+}
+
+int64_t repack_rows64(const moe_config_t &c, int32_t align)
+{
+    const int64_t pairs = (int64_t)c.max_tokens * c.num_topk;
+    const int64_t slab = (int64_t)c.num_experts * c.capacity;
+    return (pairs < slab ? pairs : slab) + (int64_t)c.num_experts * (align - 1);
+}
+
 int64_t rank_rows64(const moe_config_t &c)
 {
     return (int64_t)c.max_tokens * (c.num_topk < c.num_ranks ? c.num_topk : c.num_ranks);
@@ -525,6 +547,138 @@ moe_status_t moe_combine_reduce(const moe_config_t *cfg, int32_t num_tokens, con
     a.token_rank_row = nullptr;
     a.E = a.R = a.L = 0;
     return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_row_expert(const moe_config_t *cfg, const moe_handle_t *handle, int32_t *row_expert,
+                            void *stream)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if (row_expert == nullptr || !aligned(row_expert, 4))
+        return MOE_ERR_INVALID_ARG;
+    RowExpertArgs a;
+    a.expert_offset = handle->expert_offset;
+    a.recv_count = handle->recv_count;
+    a.E = cfg->num_experts;
+    a.rows = rows_capacity64(*cfg);
+    a.row_expert = row_expert;
+    return from_hip(launch_row_expert(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_repack_rows_capacity(const moe_config_t *cfg, int32_t align)
+{
+    if (check_config(cfg) != MOE_OK || cfg->layout != MOE_LAYOUT_MASKED || align < 1)
+        return 0;
+    const int64_t r = repack_rows64(*cfg, align);
+    return r > INT32_MAX ? 0 : (size_t)r;
+}
+
+moe_status_t moe_repack_masked_to_contiguous(const moe_config_t *cfg, int32_t align, const moe_handle_t *handle,
+                                             const void *x, const void *scale, void *out_x, void *out_scale,
+                                             int32_t *out_expert_offset, int32_t *out_row_expert, void *stream)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if (cfg->layout != MOE_LAYOUT_MASKED || align < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (repack_rows64(*cfg, align) > INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    const bool fp8 = cfg->quant != MOE_QUANT_NONE;
+    if (x == nullptr || !aligned(x, 16) || out_x == nullptr || !aligned(out_x, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 ? (scale == nullptr || !aligned(scale, 4) || out_scale == nullptr || !aligned(out_scale, 4))
+            : (scale != nullptr || out_scale != nullptr))
+        return MOE_ERR_INVALID_ARG;
+    if (out_expert_offset == nullptr || !aligned(out_expert_offset, 4) || out_row_expert == nullptr ||
+        !aligned(out_row_expert, 4))
+        return MOE_ERR_INVALID_ARG;
+    RepackArgs a;
+    a.recv_count = handle->recv_count;
+    a.in_offset = nullptr;
+    a.out_offset = out_expert_offset;
+    a.out_row_expert = out_row_expert;
+    a.x = static_cast<const uint8_t *>(x);
+    a.scale = static_cast<const uint8_t *>(scale);
+    a.out_x = static_cast<uint8_t *>(out_x);
+    a.out_scale = static_cast<uint8_t *>(out_scale);
+    a.E = cfg->num_experts;
+    a.C = cfg->capacity;
+    a.align = align;
+    a.row_bytes = fp8 ? cfg->hidden : 2 * cfg->hidden;
+    a.scale_words = scale_words32(*cfg);
+    a.out_rows = repack_rows64(*cfg, align);
+    a.to_contiguous = 1;
+    a.plan = row_plan((int32_t)repack_rows64(*cfg, 1), a.row_bytes, kAdaptWidth, kAdaptMaxIters, cfg->num_cus);
+    return from_hip(launch_repack(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_repack_contiguous_to_masked(const moe_config_t *cfg, const moe_handle_t *handle,
+                                             const int32_t *expert_offset, const uint16_t *y, uint16_t *y_masked,
+                                             void *stream)
+{
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if (cfg->layout != MOE_LAYOUT_MASKED)
+        return MOE_ERR_INVALID_ARG;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if (expert_offset == nullptr || !aligned(expert_offset, 4) || y == nullptr || !aligned(y, 16) ||
+        y_masked == nullptr || !aligned(y_masked, 16))
+        return MOE_ERR_INVALID_ARG;
+    RepackArgs a;
+    a.recv_count = handle->recv_count;
+    a.in_offset = expert_offset;
+    a.out_offset = nullptr;
+    a.out_row_expert = nullptr;
+    a.x = reinterpret_cast<const uint8_t *>(y);
+    a.scale = nullptr;
+    a.out_x = reinterpret_cast<uint8_t *>(y_masked);
+    a.out_scale = nullptr;
+    a.E = cfg->num_experts;
+    a.C = cfg->capacity;
+    a.align = 1;
+    a.row_bytes = 2 * cfg->hidden;
+    a.scale_words = 0;
+    a.out_rows = 0;
+    a.to_contiguous = 0;
+    a.plan = row_plan((int32_t)repack_rows64(*cfg, 1), a.row_bytes, kAdaptWidth, kAdaptMaxIters, cfg->num_cus);
+    return from_hip(launch_repack(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_scale_words(const moe_config_t *cfg)
+{
+    if (check_config(cfg) != MOE_OK)
+        return 0;
+    return (size_t)scale_words32(*cfg);
+}
+
+moe_status_t moe_scales_mn_major(const moe_config_t *cfg, int32_t rows, const void *scale, void *scale_mn,
+                                 void *stream)
+{
+    const moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    const int32_t S = scale_words32(*cfg);
+    if (S == 0 || rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (scale == nullptr || !aligned(scale, 4) || scale_mn == nullptr || !aligned(scale_mn, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (rows == 0)
+        return MOE_OK;
+    MnMajorArgs a;
+    a.in = static_cast<const uint32_t *>(scale);
+    a.out = static_cast<uint32_t *>(scale_mn);
+    a.rows = rows;
+    a.ld = ((int64_t)rows + 3) / 4 * 4;
+    a.S = S;
+    return from_hip(launch_scales_mn_major(a, static_cast<hipStream_t>(stream)));
 }
 
 const char *moe_status_str(moe_status_t status)

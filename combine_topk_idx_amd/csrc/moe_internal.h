@@ -131,6 +131,46 @@ struct ExpandArgs {
 constexpr int kExpandWidth = kWave * 16;  // bytes per wave iteration, 16 per lane
 constexpr int kExpandMaxIters = 8;
 
+// ---- adapters for grouped-GEMM consumers ------------------------------------
+
+struct RowExpertArgs {
+    const int32_t *expert_offset;  // [E + 1]
+    const int32_t *recv_count;     // [E]
+    int32_t E;
+    int64_t rows;
+    int32_t *row_expert;           // [rows]
+};
+
+struct RepackArgs {
+    const int32_t *recv_count;     // [E] rows received per expert (masked handle)
+    const int32_t *in_offset;      // contiguous -> masked: the contiguous segment offsets [E + 1]
+    int32_t *out_offset;           // masked -> contiguous: segment offsets written [E + 1]
+    int32_t *out_row_expert;       // masked -> contiguous: [out_rows]
+    const uint8_t *x;
+    const uint8_t *scale;
+    uint8_t *out_x;
+    uint8_t *out_scale;
+    int32_t E, C, align, row_bytes, scale_words;
+    int64_t out_rows;              // masked -> contiguous: rows of out_x / out_row_expert
+    int32_t to_contiguous;
+    RowPlan plan;                  // items over the E * C slab rows, kAdaptWidth bytes per iteration
+};
+
+struct MnMajorArgs {
+    const uint32_t *in;
+    uint32_t *out;
+    int64_t rows, ld;
+    int32_t S;
+};
+
+constexpr int kAdaptWidth = kWave * 16;  // bytes per wave iteration
+constexpr int kAdaptMaxIters = 8;
+constexpr int kTransposeTile = 64;
+
+hipError_t launch_row_expert(const RowExpertArgs &a, hipStream_t stream);
+hipError_t launch_repack(const RepackArgs &a, hipStream_t stream);
+hipError_t launch_scales_mn_major(const MnMajorArgs &a, hipStream_t stream);
+
 int device_cu_count();
 RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item,
                  int32_t num_cus, int32_t min_items_per_token = 1);

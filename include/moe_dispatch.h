@@ -310,6 +310,82 @@ moe_status_t moe_combine_partial(const moe_config_t *cfg, int32_t num_tokens, co
 moe_status_t moe_combine_reduce(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *partial,
                                 const moe_rank_handle_t *rank_handle, uint16_t *out, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Adapters for grouped-GEMM consumers.
+ *
+ * The dispatched buffers feed grouped expert GEMMs that read either the
+ * contiguous layout (prefill) or the masked slab (decode), with fp32 or
+ * packed UE8M0 scales ([A2A] Implementation: masked-slab repack kernels and
+ * GEMM adapters for contiguous prefill and masked decode).  These calls
+ * produce the forms such consumers read; none of them computes a GEMM.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Expert index of every dispatched row, the per-row group index a contiguous
+ * grouped GEMM reads:  row_expert[r] = e for rows
+ * expert_offset[e] .. expert_offset[e] + recv_count[e] - 1, and -1 for every
+ * other row (alignment padding, empty masked slots, the tail), over
+ * moe_rows_capacity(cfg) rows.  handle is a layout written by
+ * moe_dispatch_layout (or the fused call) with this cfg.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+moe_status_t moe_row_expert(const moe_config_t *cfg, const moe_handle_t *handle, int32_t *row_expert,
+                            void *stream);
+
+/* Rows a masked-to-contiguous repack writes at most:
+ * min(max_tokens*K, E*capacity) + E*(align-1).  0 for an invalid config, a
+ * contiguous cfg or align < 1. */
+size_t moe_repack_rows_capacity(const moe_config_t *cfg, int32_t align);
+
+/*
+ * Masked slab -> contiguous segments (cfg.layout must be MASKED; handle is
+ * its layout).  out_expert_offset[0] = 0 and out_expert_offset[e+1] =
+ * out_expert_offset[e] + recv_count[e] rounded up to `align`; slab row
+ * e*capacity + s (s < recv_count[e]) moves to row out_expert_offset[e] + s
+ * with its scales.
+ *   x, scale         the dispatched slab: out_x / out_scale of moe_dispatch.
+ *   out_x, out_scale [moe_repack_rows_capacity(cfg, align)] rows, same row
+ *                    formats; padding rows are not written.
+ *   out_expert_offset int32 [E+1].
+ *   out_row_expert   int32 [moe_repack_rows_capacity(cfg, align)]: as
+ *                    moe_row_expert, for the contiguous rows; written in full.
+ * Errors: MOE_ERR_INVALID_ARG (also for a contiguous cfg), MOE_ERR_HIP.
+ */
+moe_status_t moe_repack_masked_to_contiguous(const moe_config_t *cfg, int32_t align, const moe_handle_t *handle,
+                                             const void *x, const void *scale, void *out_x, void *out_scale,
+                                             int32_t *out_expert_offset, int32_t *out_row_expert,
+                                             void *stream);
+
+/*
+ * Contiguous expert outputs -> masked slab, so moe_combine can run with the
+ * masked handle: y_masked[e*capacity + s] = y[expert_offset[e] + s] for
+ * s < recv_count[e] (bf16 rows of H channels); other slab rows are not
+ * written.  expert_offset is out_expert_offset of the masked-to-contiguous
+ * repack of the same handle.
+ * Errors: MOE_ERR_INVALID_ARG (also for a contiguous cfg), MOE_ERR_HIP.
+ */
+moe_status_t moe_repack_contiguous_to_masked(const moe_config_t *cfg, const moe_handle_t *handle,
+                                             const int32_t *expert_offset, const uint16_t *y, uint16_t *y_masked,
+                                             void *stream);
+
+/* 32-bit scale words per dispatched row: H/128 (fp32), ceil(H/512) (packed
+ * UE8M0), H/128 (MXFP8: four E8M0 bytes per word); 0 for bf16 or an invalid
+ * config. */
+size_t moe_scale_words(const moe_config_t *cfg);
+
+/*
+ * Scales in MN-major order, the layout TMA-fed grouped GEMMs read: the
+ * row-major scales [rows, S] (S = moe_scale_words(cfg) 32-bit words per row,
+ * as written by the dispatch calls) become [S, ld] with
+ * scale_mn[j*ld + r] = scale[r*S + j], ld = rows rounded up to a multiple of 4
+ * (16 bytes), and the ld - rows padding entries 0.  Works on the 32-bit words,
+ * so packed UE8M0 and MXFP8 scales keep four blocks per word.
+ * Errors: MOE_ERR_INVALID_ARG (bf16 cfg, rows < 0, null or misaligned
+ * pointers), MOE_ERR_HIP.
+ */
+moe_status_t moe_scales_mn_major(const moe_config_t *cfg, int32_t rows, const void *scale, void *scale_mn,
+                                 void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *moe_status_str(moe_status_t status);
 

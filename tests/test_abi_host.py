@@ -37,7 +37,9 @@ def test_exports_every_declared_symbol(lib):
                           "moe_dispatch_layout", "moe_dispatch", "moe_dispatch_fused", "moe_combine",
                           "moe_status_str", "moe_rank_rows_capacity", "moe_rank_layout",
                           "moe_dispatch_dedup", "moe_expand", "moe_combine_partial",
-                          "moe_combine_reduce"}
+                          "moe_combine_reduce", "moe_row_expert", "moe_repack_rows_capacity",
+                          "moe_repack_masked_to_contiguous", "moe_repack_contiguous_to_masked",
+                          "moe_scale_words", "moe_scales_mn_major"}
     out = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
@@ -301,3 +303,67 @@ def test_dedup_pointer_errors(lib):
     assert _call(lib, "expand", c, 0, idx=None, send=None) == M.MOE_OK
     assert _call(lib, "combine_partial", c, 0, idx=None, y=None, w=None, partial=None) == M.MOE_OK
     assert _call(lib, "combine_reduce", c, 0, partial=None, out=None) == M.MOE_OK
+
+
+# ---- grouped-GEMM adapters ----------------------------------------------------
+
+def test_adapter_size_queries(lib):
+    m = _cfg(max_tokens=256, hidden=7168, num_experts=256, num_topk=8, num_ranks=8,
+             layout=M.LAYOUT_MASKED, capacity=256, quant=M.QUANT_FP8_F32)
+    assert M.moe_repack_rows_capacity(m, 1) == 2048
+    assert M.moe_repack_rows_capacity(m, 128) == 2048 + 256 * 127
+    small = _cfg(layout=M.LAYOUT_MASKED, capacity=3)            # E*C = 24 < T*K = 128
+    assert M.moe_repack_rows_capacity(small, 2) == 24 + 8
+    assert M.moe_repack_rows_capacity(_cfg(), 4) == 0           # contiguous cfg
+    assert M.moe_repack_rows_capacity(small, 0) == 0
+    assert M.moe_scale_words(m) == 56
+    assert M.moe_scale_words(_cfg(hidden=7168, quant=M.QUANT_FP8_UE8M0)) == 14
+    assert M.moe_scale_words(_cfg(hidden=640, quant=M.QUANT_FP8_UE8M0)) == 2
+    assert M.moe_scale_words(_cfg(hidden=7168, quant=M.QUANT_MXFP8)) == 56
+    assert M.moe_scale_words(_cfg()) == 0
+    assert lib.moe_scale_words(None) == 0
+
+
+def test_adapter_argument_errors(lib):
+    """Every call has at least one argument the host check rejects, so no
+    kernel is launched."""
+    bad = M.MOE_ERR_INVALID_ARG
+    c = _cfg()
+    m = _cfg(layout=M.LAYOUT_MASKED, capacity=4)
+    mf = _cfg(layout=M.LAYOUT_MASKED, capacity=4, quant=M.QUANT_FP8_F32)
+    h = ctypes.byref(_handle())
+    assert lib.moe_row_expert(ctypes.byref(c), h, None, None) == bad
+    assert lib.moe_row_expert(ctypes.byref(c), h, FAKE + 2, None) == bad
+    assert lib.moe_row_expert(ctypes.byref(c), None, FAKE, None) == bad
+    assert lib.moe_row_expert(ctypes.byref(_cfg(num_topk=0)), h, FAKE, None) == bad
+    hb = ctypes.byref(_handle(recv_count=None))
+    assert lib.moe_row_expert(ctypes.byref(c), hb, FAKE, None) == bad
+
+    def m2c(cfg, align=4, h=h, x=FAKE, s=None, ox=FAKE, os_=None, off=FAKE, rex=FAKE):
+        return lib.moe_repack_masked_to_contiguous(ctypes.byref(cfg), align, h, x, s, ox, os_, off, rex, None)
+    assert m2c(c) == bad                       # contiguous cfg
+    assert m2c(m, align=0) == bad
+    assert m2c(m, h=hb) == bad
+    assert m2c(m, x=None) == bad
+    assert m2c(m, ox=FAKE + 8) == bad
+    assert m2c(m, s=FAKE) == bad               # scales without FP8
+    assert m2c(mf) == bad                      # FP8 needs both scale pointers
+    assert m2c(mf, s=FAKE) == bad
+    assert m2c(m, off=None) == bad
+    assert m2c(m, rex=FAKE + 1) == bad
+
+    def c2m(cfg, h=h, off=FAKE, y=FAKE, ym=FAKE):
+        return lib.moe_repack_contiguous_to_masked(ctypes.byref(cfg), h, off, y, ym, None)
+    assert c2m(c) == bad
+    assert c2m(m, h=hb) == bad
+    assert c2m(m, off=None) == bad
+    assert c2m(m, y=FAKE + 2) == bad
+    assert c2m(m, ym=None) == bad
+
+    def mn(cfg, rows=8, s=FAKE, o=FAKE):
+        return lib.moe_scales_mn_major(ctypes.byref(cfg), rows, s, o, None)
+    assert mn(c) == bad                        # bf16: no scales
+    assert mn(mf, rows=-1) == bad
+    assert mn(mf, s=None) == bad
+    assert mn(mf, o=FAKE + 4) == bad
+    assert mn(mf, rows=0) == M.MOE_OK          # nothing to do, nothing enqueued
