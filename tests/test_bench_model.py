@@ -1,0 +1,73 @@
+"""CPU checks of bench.py's byte models and JSON helpers (no GPU needed).
+
+The algorithmic bytes per call are what the roofline fractions divide by, so
+they are pinned to hand counts of the DeepSeek-V3 prefill batch: 65,536
+kept pairs, H = 7168, 56 quantization blocks, 14 packed UE8M0 words per row.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+bench = pytest.importorskip("bench")
+from combine_topk_idx_amd import workloads as W  # noqa: E402
+
+
+def test_direct_path_bytes_deepseek_prefill():
+    wl = W.WORKLOADS["deepseekv3_prefill_T8192"]
+    ab = bench.algorithmic_bytes(wl, 65536)
+    T, K, H, N = 8192, 8, 7168, 65536
+    assert ab["layout"] == 4 * T * K + 4 * T * K + 4 * N == 786_432
+    assert ab["dispatch"] == 2 * T * H + 4 * T * K + N * (H + 56) == 591_134_720
+    assert ab["combine"] == 2 * N * H + 8 * T * K + 2 * T * H == 1_057_488_896
+    assert sum(ab.values()) == 1_649_410_048
+
+
+def test_bytes_per_format():
+    base = W.WORKLOADS["deepseekv3_prefill_T8192"]
+    T, K, H, N = 8192, 8, 7168, 65536
+    rows = {W.QUANT_NONE: 2 * H, W.QUANT_FP8_F32: H + 4 * 56, W.QUANT_FP8_UE8M0: H + 56,
+            W.QUANT_MXFP8: H + 224}
+    for q, row in rows.items():
+        ab = bench.algorithmic_bytes(base.replace(quant=q), N)
+        assert ab["dispatch"] == 2 * T * H + 4 * T * K + N * row
+        assert bench.row_and_scale_bytes(base.replace(quant=q))[0] + \
+            bench.row_and_scale_bytes(base.replace(quant=q))[1] == row
+
+
+def test_dedup_bytes_deepseek_prefill():
+    wl = W.WORKLOADS["deepseekv3_prefill_T8192"]
+    T, K, H, R, N, Q = 8192, 8, 7168, 8, 65536, 32477
+    ab = bench.dedup_bytes(wl, N, Q)
+    row = H + 56
+    assert ab["dispatch_dedup"] == 2 * T * H + 4 * T * R + Q * row
+    assert ab["expand"] == 12 * T * K + Q * row + N * row
+    assert ab["combine_partial"] == 2 * N * H + 16 * T * K + 2 * Q * H
+    assert ab["combine_reduce"] == 4 * T * R + 2 * Q * H + 2 * T * H
+
+
+def test_short_kernel_names():
+    assert bench.short_kernel("void moe::(anonymous namespace)::dispatch_rows<2>(moe::DispatchArgs)") \
+        == "dispatch_rows_fp8_ue8m0"
+    assert bench.short_kernel("void moe::(anonymous namespace)::combine_kernel<false>(moe::CombineArgs)") \
+        == "combine_kernel"
+    assert bench.short_kernel("void moe::(anonymous namespace)::combine_kernel<true>(moe::CombineArgs)") \
+        == "combine_kernel_partial"
+    assert bench.short_kernel("moe::(anonymous namespace)::layout_single(moe::LayoutArgs)") == "layout_single"
+    assert bench.short_kernel("void moe::(anonymous namespace)::repack_kernel<true>(moe::RepackArgs)") \
+        == "repack_to_contiguous"
+
+
+def test_library_hash_is_stable():
+    assert bench.library_hash() == bench.library_hash()
+    assert len(bench.library_hash()) == 64
+
+
+def test_bench_refuses_more_than_one_gpu(tmp_path):
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "one GPU" in r.stderr
