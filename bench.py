@@ -452,9 +452,12 @@ def summarize(run_dir, calib_mib):
     print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
 
 
-def cpu_baseline(wl, inp, y, max_tokens):
+def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
     """The CPU oracle (single thread, as it stands) on a bounded sample: the
-    first `max_tokens` tokens of the same batch, layout + dispatch + combine."""
+    first `max_tokens` tokens of the same batch, layout + dispatch + combine.
+    When the sample is the whole batch and `gpu` holds the benchmark's final
+    outputs (host copies), they are checked against the oracle's: layout and
+    dispatched bytes bit for bit, combine within |g - o| <= 1e-2 |o| + 1e-5 S."""
     import oracle
     T = min(wl.T, max_tokens)
     sub = wl.replace(T=T)
@@ -463,12 +466,38 @@ def cpu_baseline(wl, inp, y, max_tokens):
     oracle._load()
     t0 = time.perf_counter()
     h = oracle.dispatch_layout(idx, wl.E, wl.R, wl.layout, wl.align, wl.capacity, rows_cap=rows)
-    oracle.dispatch(x, h["pair_to_row"], wl.K, wl.quant, rows)
-    oracle.combine(y[:rows], w, h["pair_to_row"])
+    ox, osc, _ = oracle.dispatch(x, h["pair_to_row"], wl.K, wl.quant, rows)
+    out = oracle.combine(y[:rows], w, h["pair_to_row"])
     dt = time.perf_counter() - t0
-    return {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {T} of {wl.T} tokens of the same batch, one layout+dispatch+combine "
-                      f"pass, single-threaded C oracle ({dt:.1f} s)"}
+    res = {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {T} of {wl.T} tokens of the same batch, one layout+dispatch+combine "
+                     f"pass, single-threaded C oracle ({dt:.1f} s)"}
+    if gpu is not None and T == wl.T:
+        check = {}
+        check["layout_bit_exact"] = all(np.array_equal(gpu[k][:h[k].size], h[k]) for k in (
+            "expert_count", "recv_count", "expert_offset", "rank_offset", "pair_to_row", "row_to_pair", "status"))
+        kept = h["row_to_pair"] >= 0
+        check["dispatch_bit_exact"] = bool(
+            np.array_equal(gpu["out_x"].reshape(rows, -1)[kept], ox.view(np.uint8).reshape(rows, -1)[kept])
+            and (osc is None or np.array_equal(gpu["out_scale"].reshape(rows, -1)[kept],
+                                               osc.view(np.uint8).reshape(rows, -1)[kept])))
+        g = W.bf16_bits_to_f32(gpu["out"]).astype(np.float64)
+        o = W.bf16_bits_to_f32(out).astype(np.float64)
+        diff = g != o
+        check["combine_unequal_elements"] = int(diff.sum())
+        if diff.any():  # tolerance on the differing elements only
+            p2r = h["pair_to_row"].reshape(T, wl.K)
+            tt, jj = np.nonzero(diff)
+            S = np.zeros(tt.size)
+            for k in range(wl.K):
+                r = p2r[tt, k]
+                ok = r >= 0
+                S[ok] += np.abs(w[tt[ok], k] * W.bf16_bits_to_f32(y[r[ok], jj[ok]]))
+            check["combine_within_tolerance"] = bool(np.all(np.abs(g[diff] - o[diff]) <= 1e-2 * np.abs(o[diff]) + 1e-5 * S))
+        else:
+            check["combine_within_tolerance"] = True
+        res["oracle_check"] = check
+    return res
 
 
 def main():
@@ -700,8 +729,12 @@ def main():
                  "status": status.tolist(), "copy_ceiling_gbs": copy_gbs},
     }
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(wl, inp, y, args.cpu_sample_tokens)
+        log("[bench] cpu baseline (oracle), and the last step's outputs against it")
+        gpu = {k: v.cpu().numpy() for k, v in bufs.handle.tensors().items()}
+        gpu["out_x"] = bufs.out_x.cpu().numpy().view(np.uint8)
+        gpu["out_scale"] = None if bufs.out_scale is None else bufs.out_scale.cpu().numpy().view(np.uint8)
+        gpu["out"] = d_out.cpu().numpy().view(np.uint16)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, y, args.cpu_sample_tokens, gpu)
     print(json.dumps(result), flush=True)
 
 

@@ -404,3 +404,67 @@ def test_quant_sweep_all_bf16_magnitudes():
         w = np.full((T, 2), 0.5, np.float32)
         y = W.f32_to_bf16_bits(rng.standard_normal((wl.rows_capacity, H)).astype(np.float32))
         check_parity(wl, idx, w, x, y, make_cfg(wl), f"sweep quant {quant}", fused=True)
+
+
+def test_determinism_ten_runs():
+    """Ten runs of the headline step (fused dispatch + combine) leave every
+    output bitwise identical, compared on the device."""
+    wl = W.WORKLOADS[W.HEADLINE]
+    _say(f"determinism over 10 runs: {wl.name}")
+    inp = W.make_inputs(wl)
+    y = W.expert_outputs(wl, inp)
+    cfg = make_cfg(wl)
+    bufs = M.DispatchBuffers(cfg, row_weight=True)
+    d_idx = torch.from_numpy(inp.topk_idx).cuda()
+    d_w = torch.from_numpy(inp.topk_w).cuda()
+    d_x = torch.from_numpy(inp.x.view(np.int16)).cuda()
+    d_y = torch.from_numpy(y.view(np.int16)).cuda()
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+    first = None
+    for run in range(10):
+        for t in (bufs.out_x, bufs.out_scale, bufs.out_row_weight, out):
+            t.view(torch.uint8).fill_(SENT)
+        M.moe_dispatch_fused(cfg, wl.T, d_idx, d_x, d_w, bufs.handle, bufs.workspace, bufs.out_x,
+                             bufs.out_scale, bufs.out_row_weight)
+        M.moe_combine(cfg, wl.T, d_y, d_w, bufs.handle, out)
+        snap = [t.clone() for t in list(bufs.handle.tensors().values()) +
+                [bufs.out_x, bufs.out_scale, bufs.out_row_weight, out]]
+        torch.cuda.synchronize()
+        if first is None:
+            first = snap
+        else:
+            for a, b in zip(first, snap):
+                assert torch.equal(a, b), f"run {run} differs from run 0"
+
+
+def test_fp32_scale_sweep_non_power_of_two():
+    """The fp32-scale path with scales that are not powers of two: every
+    bf16 value up to 448 c in blocks whose maximum is 448 c, so x / s lands on
+    fp32 values with mantissa bits beyond bf16, near E4M3 rounding ties
+    included; the hardware conversion must match the oracle's encoder."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = W.bf16_bits_to_f32(b)
+    rng = np.random.default_rng(78)
+    H = 7168
+    blocks = []
+    for c in (1.1, 1.37, 1.5, 1.9921875, 3.0, 0.7, 1e-3, 1e5):
+        amax = np.float32(448.0 * c)
+        amax_bf = W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.array([amax], np.float32)))[0]
+        vals = f[np.isfinite(f) & (np.abs(f) <= amax_bf)]
+        per = 127
+        nblk = -(-vals.size // per)
+        pad = np.zeros(nblk * per, np.float32)
+        pad[:vals.size] = rng.permutation(vals)
+        blocks.append(np.concatenate([np.full((nblk, 1), amax_bf, np.float32), pad.reshape(nblk, per)], 1))
+    allb = np.concatenate(blocks).reshape(-1)
+    T = -(-allb.size // H)
+    xf = np.zeros(T * H, np.float32)
+    xf[:allb.size] = allb
+    x = W.f32_to_bf16_bits(xf.reshape(T, H))
+    _say(f"fp32-scale sweep with non-power-of-two scales, T={T}")
+    wl = W.Workload("sweep_f32", T=T, H=H, E=4, K=2, R=2, layout=W.LAYOUT_CONTIGUOUS, align=1,
+                    quant=W.QUANT_FP8_F32)
+    idx = np.stack([np.arange(T) % 4, (np.arange(T) + 1) % 4], 1).astype(np.int32)
+    w = np.full((T, 2), 0.5, np.float32)
+    y = W.f32_to_bf16_bits(rng.standard_normal((wl.rows_capacity, H)).astype(np.float32))
+    check_parity(wl, idx, w, x, y, make_cfg(wl), "fp32-scale sweep", fused=False)
