@@ -10,7 +10,7 @@
 namespace moe {
 
 constexpr int kWave = 64;             // CDNA wavefront width
-constexpr int kBlockThreads = 256;    // 4 waves per workgroup for every kernel
+constexpr int kBlockThreads = 256;    // 4 waves per workgroup for the row kernels
 constexpr int kWavesPerBlock = kBlockThreads / kWave;
 constexpr int kQuantGroup = 128;      // 1x128 activation quantization group
 constexpr int kMaxTopk = 32;
@@ -153,7 +153,7 @@ struct RepackArgs {
     int32_t E, C, align, row_bytes, scale_words;
     int64_t out_rows;              // masked -> contiguous: rows of out_x / out_row_expert
     int32_t to_contiguous;
-    RowPlan plan;                  // items over the E * C slab rows, kAdaptWidth bytes per iteration
+    RowPlan plan;                  // items over the kept rows (at most min(T*K, E*C)), kAdaptWidth bytes each
 };
 
 struct MnMajorArgs {
