@@ -58,6 +58,8 @@ MASKED = [
     ("skewed_prefill_T16384_masked_bf16", dict(T=3000)),
     ("deepseekv3_decode_T256", dict(name="decode_mxfp8", quant=W.QUANT_MXFP8, H=1024)),
     ("deepseekv3_decode_T256", dict(name="decode_ue8m0_c5", quant=W.QUANT_FP8_UE8M0, capacity=5, H=640)),
+    ("deepseekv3_decode_T256", dict(name="wide_bf16", quant=W.QUANT_NONE, T=32, H=32768, capacity=8)),
+    ("deepseekv3_decode_T256", dict(name="wide_mxfp8", quant=W.QUANT_MXFP8, T=32, H=32768, capacity=8)),
 ]
 
 

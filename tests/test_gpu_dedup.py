@@ -205,6 +205,8 @@ SMALL = [
     ("masked_drops_ue8m0", "deepseekv3_decode_T256", dict(T=300, H=512, capacity=3,
                                                           quant=W.QUANT_FP8_UE8M0)),
     ("mxfp8_contig", "deepseekv3_prefill_T8192", dict(T=500, H=1024, quant=W.QUANT_MXFP8)),
+    ("wide_rows_ue8m0", "tiny_T64", dict(T=40, E=16, R=4, K=4, H=32768, quant=W.QUANT_FP8_UE8M0, align=4)),
+    ("wide_rows_bf16", "tiny_T64", dict(T=40, E=16, R=4, K=4, H=32768, align=4)),
     ("many_chunks_T140000", "tiny_T64", dict(T=140000, E=64, R=16, K=2, H=64)),
     ("lds_budget_T1100000_R32", "tiny_T64", dict(T=1100000, E=32, R=32, K=1, H=8)),
 ]

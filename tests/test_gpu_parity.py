@@ -256,6 +256,10 @@ SMALL = [
     (3000, 128, 600, 4, 8, W.LAYOUT_CONTIGUOUS, 2, 1, W.QUANT_FP8_UE8M0),  # E > 512: 8-wave layout blocks
     (5000, 256, 2048, 6, 16, W.LAYOUT_MASKED, 1, 3, W.QUANT_FP8_F32),     # E = 2048: 4-wave blocks
     (140000, 8, 64, 8, 8, W.LAYOUT_CONTIGUOUS, 4, 1, W.QUANT_NONE),       # > 1M pairs: multi-tile waves
+    (64, 32768, 16, 4, 4, W.LAYOUT_CONTIGUOUS, 4, 1, W.QUANT_FP8_UE8M0),  # wide rows: multi-iteration items
+    (64, 32768, 16, 4, 4, W.LAYOUT_CONTIGUOUS, 4, 1, W.QUANT_NONE),
+    (48, 32768, 16, 4, 4, W.LAYOUT_MASKED, 1, 9, W.QUANT_MXFP8),
+    (33, 20480, 16, 6, 2, W.LAYOUT_MASKED, 1, 20, W.QUANT_FP8_F32),       # 160 blocks: 40 UE8M0-size words
 ]
 
 
