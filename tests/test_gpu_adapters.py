@@ -1,12 +1,12 @@
 """GPU parity of the grouped-GEMM adapters, through the C ABI.
 
-Per case the GPU dispatch layout and dispatch run first (their parity is
-covered elsewhere); then per-row experts, the masked-to-contiguous repack
-(rows, scales, offsets, per-row experts), the contiguous-to-masked repack of
-expert outputs and the MN-major scale transpose are each compared with the
-CPU oracle applied to the same inputs, byte for byte, on sentinel-filled
-buffers inside guard bands.  A combine through the repacked outputs must equal
-the combine of the same rows written in the slab.
+Per case the GPU runs its dispatch layout and dispatch, then the adapter
+under test on its own results; the oracle runs its own layout and dispatch of
+the same seeded inputs, then its adapter.  Per-row experts, the
+masked-to-contiguous repack (rows, scales, offsets, per-row experts), the
+contiguous-to-masked repack of seeded expert outputs and the MN-major scale
+transpose are compared byte for byte, on sentinel-filled buffers inside guard
+bands; a combine through the repacked slab must equal the oracle's.
 
 Every test prints the case it runs before touching the GPU.
 """
@@ -40,15 +40,26 @@ def _inputs(wl):
 
 
 def _dispatch_on_gpu(wl, cfg, idx, x):
-    """Layout + dispatch on the GPU; returns the handle and the dispatched rows/scales."""
+    """Layout + dispatch on the GPU into zero-filled buffers; returns them."""
     T = idx.shape[0]
     bufs = M.DispatchBuffers(cfg)
+    bufs.out_x.zero_()
+    if bufs.out_scale is not None:
+        bufs.out_scale.zero_()
     d_idx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
     d_x = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
     M.moe_dispatch_layout(cfg, T, d_idx, bufs.handle, bufs.workspace)
     M.moe_dispatch(cfg, T, d_x, None, bufs.handle, bufs.out_x, bufs.out_scale)
     torch.cuda.synchronize()
     return bufs
+
+
+def _dispatch_on_oracle(wl, cfg, idx, x):
+    """The oracle's layout and dispatch of the same inputs into zero-filled buffers."""
+    rows = M.moe_rows_capacity(cfg)
+    h = oracle.dispatch_layout(idx, wl.E, wl.R, wl.layout, wl.align, wl.capacity, rows_cap=rows)
+    ox, osc, _ = oracle.dispatch(x, h["pair_to_row"], wl.K, wl.quant, rows)
+    return h, ox, osc
 
 
 MASKED = [
@@ -73,11 +84,12 @@ def test_repack_round_trip(base, kw, align):
     E, C, H = wl.E, wl.capacity, wl.H
     fp8 = wl.quant != W.QUANT_NONE
     bufs = _dispatch_on_gpu(wl, cfg, idx, x)
-    recv = bufs.handle.recv_count.cpu().numpy()
+    h, mx, ms = _dispatch_on_oracle(wl, cfg, idx, x)
+    recv = h["recv_count"]
     mrows = E * C
     crows = M.moe_repack_rows_capacity(cfg, align)
 
-    # masked -> contiguous
+    # masked -> contiguous: the GPU repacks its dispatch, the oracle repacks its own
     eb = 1 if fp8 else 2
     out_x = Guarded(crows * H * eb, torch.uint8 if fp8 else torch.int16, (crows, H))
     out_s = scale_guard(wl, crows) if fp8 else None
@@ -87,13 +99,10 @@ def test_repack_round_trip(base, kw, align):
                                       bufs.out_scale, out_x.view, None if out_s is None else out_s.view,
                                       out_off.view, out_rex.view)
     torch.cuda.synchronize()
-    mx = bufs.out_x.cpu().numpy().view(np.uint8).reshape(mrows, -1)
-    ms = None if bufs.out_scale is None else bufs.out_scale.cpu().numpy().view(np.uint8).reshape(mrows, -1)
     ox = _sentinel(crows * H * eb)
     osc = _sentinel(out_s.nbytes) if fp8 else None
     _, _, off, rex = oracle.repack_masked_to_contiguous(
-        mx.view(np.uint16) if not fp8 else mx, oracle_scale_view(wl.quant, ms, mrows) if fp8 else None,
-        recv, C, align, wl.quant, crows,
+        mx, ms, recv, C, align, wl.quant, crows,
         out_x=ox.view(np.uint8 if fp8 else np.uint16).reshape(crows, H),
         out_scale=oracle_scale_view(wl.quant, osc, crows) if fp8 else None)
     assert np.array_equal(out_off.host().view(np.int32), off), "offsets differ"
@@ -102,7 +111,7 @@ def test_repack_round_trip(base, kw, align):
     if fp8:
         assert np.array_equal(out_s.host(), osc), "repacked scales differ"
 
-    # contiguous -> masked, on stand-in expert outputs in the contiguous layout
+    # contiguous -> masked, on seeded stand-in expert outputs in the contiguous layout
     rng = np.random.default_rng(int(align) + wl.seed)
     y_c = W.f32_to_bf16_bits(rng.standard_normal((crows, H)).astype(np.float32))
     d_yc = torch.from_numpy(y_c.view(np.int16)).cuda()
@@ -114,14 +123,13 @@ def test_repack_round_trip(base, kw, align):
     got = y_m.host().view(np.uint16).reshape(mrows, H)
     assert np.array_equal(got, ref), "slab rows differ"
 
-    # combine through the slab (masked handle) equals the oracle's combine there
+    # combine through the slab (masked handle) against the oracle's combine of its slab
     T = idx.shape[0]
     d_w = torch.from_numpy(w).cuda()
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     M.moe_combine(cfg, T, y_m.view, d_w, bufs.handle, out)
     torch.cuda.synchronize()
-    p2r = bufs.handle.pair_to_row.cpu().numpy()[:T * wl.K]
-    want = oracle.combine(ref, w, p2r)   # combine reads kept rows only, all of them written
+    want = oracle.combine(ref, w, h["pair_to_row"])   # combine reads kept rows only, all of them written
     assert np.array_equal(out.cpu().numpy().view(np.uint16), want), "combine through the slab differs"
     print(f"  kept rows {int(recv.sum())}, contiguous rows used {int(off[-1])} of {crows}", flush=True)
 
@@ -165,6 +173,7 @@ def test_scales_mn_major(name, rows):
     g.view.view(torch.uint8).fill_(SENT)
     M.moe_scales_mn_major(cfg, n, bufs.out_scale, g.view)
     torch.cuda.synchronize()
-    words = bufs.out_scale.cpu().numpy().view(np.uint32).reshape(bufs.rows, S)[:n]
+    _, _, osc = _dispatch_on_oracle(wl, cfg, idx, x)   # the oracle's scales of the same inputs
+    words = np.ascontiguousarray(osc).view(np.uint32).reshape(bufs.rows, S)[:n]
     want = oracle.scales_mn_major(words)
     assert np.array_equal(g.host().view(np.uint32).reshape(S, ld), want)
