@@ -49,8 +49,8 @@
  *     scales).
  *
  * The pages leave row order, alignment, overflow handling, scale formulas and
- * rounding open; the readings taken here are listed in the design doc and in the
- * comments of each function.  Every function below is pinned by a CPU test
+ * rounding open; the readings taken here are stated in the comments of each
+ * function.  Every function below is pinned by a CPU test
  * (brute force, closed forms, library routines, exhaustive codec sweeps or
  * hand-worked fixtures); none is "parity unpinned".
  */
