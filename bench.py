@@ -348,7 +348,7 @@ def summarize(run_dir, calib_mib):
     section = wl.name + (":dedup" if dedup else ":adapters" if adapters else "")
     built = bench.get("library_sha256")
     if built is None:
-        raise SystemExit("bench.json names no library_sha256: rerun the benchmark with this build")
+        raise SystemExit("bench.json names no library_sha256: rerun the benchmark with the current library")
     algo = kernel_bytes(bench)
 
     stats = read_csv(find_file(os.path.join(run_dir, "prof_bench"), "kernel_stats.csv"))
