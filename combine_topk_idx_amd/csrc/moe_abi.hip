@@ -6,6 +6,8 @@
 // count per device.
 #include <limits.h>
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -220,19 +222,21 @@ moe_status_t prepare_dispatch(const moe_config_t *cfg, int32_t num_tokens, const
 
 }  // namespace
 
+// Compute units of the current device, asked once per device; calls from
+// several host threads may race to fill an entry, all with the same value.
 int device_cu_count()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Work items: (token, run of iterations).  Each token row has n_iters
