@@ -105,22 +105,28 @@ __device__ inline void fill_unused_rows(const LayoutArgs &a, const int32_t *tot,
         a.h.row_to_pair[r] = -1;
 }
 
-// Block 0 only: counts, offsets, rank offsets and status.  `invalid` is the
-// total of invalid ids (valid in thread 0).
+// Counts and offsets of this block's slice of the experts (every block has
+// all of them in LDS); block 0 also writes the rank offsets, expert_offset[E]
+// and the status.  `invalid` is the total of invalid ids (valid in thread 0).
 __device__ inline void publish(const LayoutArgs &a, const int32_t *tot, const int32_t *off, int32_t *red,
                                int32_t invalid)
 {
     const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nwaves = blockDim.x / kWave;
     const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
-    int32_t overflow = 0;
-    for (int e = tid; e < E; e += blockDim.x) {
+    const int per = (E + a.nblocks - 1) / a.nblocks;
+    const int e0 = min(E, (int)blockIdx.x * per), e1 = min(E, e0 + per);
+    for (int e = e0 + tid; e < e1; e += blockDim.x) {
         a.h.expert_count[e] = tot[e];
         a.h.recv_count[e] = contiguous ? tot[e] : min(tot[e], a.capacity);
         a.h.expert_offset[e] = off[e];
-        if (!contiguous)
-            overflow += max(0, tot[e] - a.capacity);
     }
+    if (blockIdx.x != 0)
+        return;
+    int32_t overflow = 0;
+    if (!contiguous)
+        for (int e = tid; e < E; e += blockDim.x)
+            overflow += max(0, tot[e] - a.capacity);
     for (int r = tid; r <= a.R; r += blockDim.x)
         a.h.rank_offset[r] = off[r * a.L];
     for (int d = kWave / 2; d > 0; d >>= 1)
@@ -151,7 +157,8 @@ __host__ __device__ inline size_t single_layout_lds_words(int32_t E, int waves)
 // atomics: all pairs in the low word, pairs before the block in the high
 // word), ranks its own pairs with a ballot match per run and an LDS scan over
 // its waves, derives the segment offsets, writes both maps for its pairs,
-// fills its share of unused rows, and block 0 publishes counts and status.
+// fills its share of unused rows, and publishes its slice of the counts and
+// offsets (block 0 also the rank offsets and status).
 // When rows_out is given, rows_out[i] receives the row of the block's pair i.
 __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, int32_t *red, int32_t *rows_out)
 {
@@ -243,10 +250,9 @@ __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, in
             rows_out[p - c0] = row;
     }
 
-    // 5. rows that hold no pair; 6. block 0 publishes
+    // 5. rows that hold no pair; 6. counts and offsets, a slice per block
     fill_unused_rows(a, tot, off);
-    if (blockIdx.x == 0)
-        publish(a, tot, off, red, invalid);
+    publish(a, tot, off, red, invalid);
 }
 
 // ---------------------------------------------------------------------------

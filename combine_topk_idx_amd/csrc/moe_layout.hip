@@ -28,7 +28,8 @@
 //                  thread) and writes the rows.
 // Both end with the same steps: segment offsets by a block-wide scan, the
 // pair <-> row maps, padding rows filled with -1 (one expert per wave over
-// the grid), and block 0 publishing counts, offsets and status.
+// the grid), and the counts and offsets published a slice of experts per
+// block (block 0 adds the rank offsets and status).
 #include "moe_device.h"
 
 namespace moe {
@@ -260,10 +261,9 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
         }
     }
 
-    // 4. rows that hold no pair; 5. block 0 publishes
+    // 4. rows that hold no pair; 5. counts and offsets, a slice per block
     fill_unused_rows(a, tot, off);
-    if (blk == 0)
-        publish(a, tot, off, red, tot[E]);
+    publish(a, tot, off, red, tot[E]);
 }
 
 // ---- schedule 1: one launch ---------------------------------------------------
