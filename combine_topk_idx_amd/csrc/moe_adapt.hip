@@ -16,33 +16,27 @@ namespace moe {
 namespace {
 
 // Exclusive scan of recv_count rounded up to `align`, into off[0..E] in LDS.
-// Block-wide; ends with a barrier.
+// Block-wide (kBlockThreads threads; red holds kWavesPerBlock words); ends
+// with a barrier.
 __device__ inline void padded_offsets(const int32_t *recv_count, int32_t E, int32_t align, int32_t *off,
                                       int32_t *red)
 {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int per = (E + kBlockThreads - 1) / kBlockThreads;
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
     int32_t local = 0;
     for (int e = e0; e < e1; ++e)
         local += (recv_count[e] + align - 1) / align * align;
-    int32_t incl = local;
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t v = __shfl_up(incl, d);
-        if (lane >= d)
-            incl += v;
-    }
+    const int32_t incl = dev::wave_inclusive_sum(local);
     if (lane == kWave - 1)
         red[wave] = incl;
     __syncthreads();
-    int32_t run = incl - local;
-    for (int w = 0; w < wave; ++w)
-        run += red[w];
+    int32_t run = dev::sum_before<kWavesPerBlock>(red, wave) + incl - local;
     for (int e = e0; e < e1; ++e) {
         off[e] = run;
         run += (recv_count[e] + align - 1) / align * align;
     }
-    if (tid == (int)blockDim.x - 1)
+    if (tid == kBlockThreads - 1)
         off[E] = run;
     __syncthreads();
 }
@@ -75,8 +69,8 @@ __device__ inline void fill_row_expert(const int32_t *off, const int32_t *recv_c
                                        int32_t *row_expert)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gwave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t gwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t gwave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + threadIdx.x / kWave;
+    const int64_t gwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
     for (int64_t e = gwave; e < E; e += gwaves) {
         const int32_t used = recv_count[e];
         for (int32_t r = off[e] + lane; r < off[e + 1]; r += kWave)
@@ -106,10 +100,10 @@ __global__ __launch_bounds__(kBlockThreads) void repack_kernel(RepackArgs a)
     if (TO_CONTIGUOUS) {
         padded_offsets(a.recv_count, a.E, a.align, off, red);
         if (blockIdx.x == 0)
-            for (int e = threadIdx.x; e <= a.E; e += blockDim.x)
+            for (int e = threadIdx.x; e <= a.E; e += kBlockThreads)
                 a.out_offset[e] = off[e];
     } else {
-        for (int e = threadIdx.x; e <= a.E; e += blockDim.x)
+        for (int e = threadIdx.x; e <= a.E; e += kBlockThreads)
             off[e] = a.in_offset[e];
         __syncthreads();
     }

@@ -33,42 +33,72 @@ __device__ __forceinline__ uint64_t match_expert(int32_t e, bool routed, int nbi
     return routed ? m : 0ull;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave without LDS: Hillis-Steele
+// shifts of 1, 2, 4, 8 inside each row of 16 lanes (row_shr; lanes with no
+// source add 0), then the row totals carried across rows (row_bcast:15 into
+// rows 1 and 3, row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// Sum of red[w] over the waves w before `wave` (red holds N entries); the
+// reads are independent, so they are all in flight at once.
+template <int N>
+__device__ __forceinline__ int32_t sum_before(const int32_t *red, int wave)
+{
+    int32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < N; ++w)
+        s += w < wave ? red[w] : 0;
+    return s;
+}
+
 // ---------------------------------------------------------------------------
-// Layout steps (a block of blockDim.x / 64 waves; a.nblocks blocks)
+// Layout steps (a block of NT threads, NT = 0: blockDim.x; a.nblocks blocks).
+// A compile-time NT keeps the block size out of memory: reading blockDim.x
+// costs a load from the dispatch packet that the first loads wait behind.
 // ---------------------------------------------------------------------------
+
+template <int NT>
+__device__ __forceinline__ int block_threads()
+{
+    return NT > 0 ? NT : (int)blockDim.x;
+}
 
 // off[0..E] = segment starts: exclusive scan of align-padded totals
 // (contiguous) or e * capacity (masked).  Block-wide; ends with a barrier.
+// `red` holds kMaxBlockWaves words.
+template <int NT>
 __device__ inline void segment_offsets(const LayoutArgs &a, const int32_t *tot, int32_t *off, int32_t *red)
 {
     const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int nt = block_threads<NT>();
     if (a.layout == MOE_LAYOUT_CONTIGUOUS) {
-        const int per = (E + blockDim.x - 1) / blockDim.x;
+        const int per = (E + nt - 1) / nt;
         const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
         int32_t local = 0;
         for (int e = e0; e < e1; ++e)
             local += (tot[e] + a.align - 1) / a.align * a.align;
-        int32_t incl = local;  // inclusive scan over the wave
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int32_t v = __shfl_up(incl, d);
-            if (lane >= d)
-                incl += v;
-        }
+        const int32_t incl = wave_inclusive_sum(local);
         if (lane == kWave - 1)
             red[wave] = incl;
         __syncthreads();
-        int32_t base = 0;
-        for (int w = 0; w < wave; ++w)
-            base += red[w];
-        int32_t run = base + incl - local;
+        int32_t run = sum_before<kMaxBlockWaves>(red, wave) + incl - local;
         for (int e = e0; e < e1; ++e) {
             off[e] = run;
             run += (tot[e] + a.align - 1) / a.align * a.align;
         }
-        if (tid == blockDim.x - 1)
+        if (tid == nt - 1)
             off[E] = run;
     } else {
-        for (int e = tid; e <= E; e += blockDim.x)
+        for (int e = tid; e <= E; e += nt)
             off[e] = e * a.capacity;
     }
     __syncthreads();
@@ -86,9 +116,10 @@ __device__ __forceinline__ int32_t row_of(const LayoutArgs &a, const int32_t *of
 // row_to_pair = -1 for rows that hold no pair: the padding after each
 // expert's rows (one expert per wave over the grid) and a slice of the tail
 // past the last segment per wave.
+template <int NT>
 __device__ inline void fill_unused_rows(const LayoutArgs &a, const int32_t *tot, const int32_t *off)
 {
-    const int lane = threadIdx.x & (kWave - 1), nwaves = blockDim.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), nwaves = block_threads<NT>() / kWave;
     const int gwave = blockIdx.x * nwaves + (int)(threadIdx.x / kWave);
     const int gwaves = a.nblocks * nwaves;
     const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
@@ -107,71 +138,77 @@ __device__ inline void fill_unused_rows(const LayoutArgs &a, const int32_t *tot,
 
 // Counts and offsets of this block's slice of the experts (every block has
 // all of them in LDS); block 0 also writes the rank offsets, expert_offset[E]
-// and the status.  `invalid` is the total of invalid ids (valid in thread 0).
-__device__ inline void publish(const LayoutArgs &a, const int32_t *tot, const int32_t *off, int32_t *red,
+// and the status.  `overflow` (pairs dropped by the masked capacity) and
+// `invalid` (ids outside [-1, E)) are read in thread 0 of block 0 only.
+template <int NT>
+__device__ inline void publish(const LayoutArgs &a, const int32_t *tot, const int32_t *off, int32_t overflow,
                                int32_t invalid)
 {
-    const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int nwaves = blockDim.x / kWave;
+    const int E = a.E, tid = threadIdx.x, nt = block_threads<NT>();
     const bool contiguous = a.layout == MOE_LAYOUT_CONTIGUOUS;
     const int per = (E + a.nblocks - 1) / a.nblocks;
     const int e0 = min(E, (int)blockIdx.x * per), e1 = min(E, e0 + per);
-    for (int e = e0 + tid; e < e1; e += blockDim.x) {
+    for (int e = e0 + tid; e < e1; e += nt) {
         a.h.expert_count[e] = tot[e];
         a.h.recv_count[e] = contiguous ? tot[e] : min(tot[e], a.capacity);
         a.h.expert_offset[e] = off[e];
     }
     if (blockIdx.x != 0)
         return;
-    int32_t overflow = 0;
-    if (!contiguous)
-        for (int e = tid; e < E; e += blockDim.x)
-            overflow += max(0, tot[e] - a.capacity);
-    for (int r = tid; r <= a.R; r += blockDim.x)
+    for (int r = tid; r <= a.R; r += nt)
         a.h.rank_offset[r] = off[r * a.L];
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        overflow += __shfl_xor(overflow, d);
-    __syncthreads();  // `red` is reused
-    if (lane == 0)
-        red[wave] = overflow;
-    __syncthreads();
     if (tid == 0) {
-        int32_t o = 0;
-        for (int w = 0; w < nwaves; ++w)
-            o += red[w];
         a.h.expert_offset[E] = off[E];
-        a.h.status[0] = o;
+        a.h.status[0] = overflow;
         a.h.status[1] = invalid;
     }
+}
+
+// Adds the pairs that the masked capacity drops from this thread's experts
+// (tot[e] > capacity, rare) into *over with LDS atomics; a later barrier
+// orders them before *over is read.
+template <int NT>
+__device__ __forceinline__ void count_overflow(const LayoutArgs &a, const int32_t *tot, int32_t *over)
+{
+    if (a.layout == MOE_LAYOUT_CONTIGUOUS)
+        return;
+    for (int e = threadIdx.x; e < a.E; e += block_threads<NT>())
+        if (tot[e] > a.capacity)
+            atomicAdd(over, tot[e] - a.capacity);
 }
 
 // LDS int32 words the one-launch layout needs.
 __host__ __device__ inline size_t single_layout_lds_words(int32_t E, int waves)
 {
-    return (size_t)2 * E /* 64-bit histogram */ + E /* tot */ + (E + 1) /* off */ + (size_t)waves * E /* cnt */;
+    return (size_t)2 * E /* pre, post */ + E /* tot */ + (E + 1) /* off */ + (size_t)waves * E /* cnt */ +
+           2 /* invalid, overflow */;
 }
 
-// The whole layout for one block that needs nothing from other blocks: the
-// block owns pairs [blk*chunk, blk*chunk + chunk) (chunk <= 64 * waves, one
-// run of 64 pairs per wave).  It histograms ALL pairs itself (64-bit LDS
-// atomics: all pairs in the low word, pairs before the block in the high
-// word), ranks its own pairs with a ballot match per run and an LDS scan over
-// its waves, derives the segment offsets, writes both maps for its pairs,
-// fills its share of unused rows, and publishes its slice of the counts and
-// offsets (block 0 also the rank offsets and status).
-// When rows_out is given, rows_out[i] receives the row of the block's pair i.
+// The whole layout for one block of kSingleThreads threads that needs nothing
+// from other blocks: the block owns pairs [blk*chunk, blk*chunk + chunk) (chunk <= 64 * waves, one
+// run of 64 pairs per wave).  It histograms ALL pairs itself (32-bit LDS
+// atomics, into `pre` for pairs before the block and `post` for the rest),
+// ranks its own pairs with a ballot match per run and the counts of earlier
+// waves, derives the segment offsets, writes both maps for its pairs, fills
+// its share of unused rows, and publishes its slice of the counts and offsets
+// (block 0 also the rank offsets and status).  Invalid ids and dropped pairs
+// are rare: lanes that have some add them into LDS counters with atomics.
+// `red` holds kMaxBlockWaves words.  When rows_out is given, rows_out[i]
+// receives the row of the block's pair i.
 __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, int32_t *red, int32_t *rows_out)
 {
+    constexpr int NT = kSingleThreads;
     const int E = a.E;
-    unsigned long long *hist = reinterpret_cast<unsigned long long *>(lds);  // [E]
-    int32_t *tot = lds + 2 * E;  // [E]
+    int32_t *pre = lds;          // [E] pairs before the block, then slot bases
+    int32_t *post = pre + E;     // [E] pairs from the block on
+    int32_t *tot = post + E;     // [E]
     int32_t *off = tot + E;      // [E+1]
     int32_t *cnt = off + E + 1;  // [waves][E] per-wave counts, then per-wave slot bases
-
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int nwaves = blockDim.x / kWave;
+    constexpr int nwaves = NT / kWave;
+    int32_t *misc = cnt + nwaves * E;  // [0] invalid ids, [1] dropped pairs
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
     const int64_t c1 = min(a.P, c0 + a.chunk);
 
@@ -179,37 +216,49 @@ __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, in
     const int64_t p = c0 + (int64_t)wave * kWave + lane;
     const bool own = p < c1;
     const int32_t e_own = own ? a.topk_idx[p] : -1;
-    for (int i = tid; i < E; i += blockDim.x)
-        hist[i] = 0ull;
-    for (int i = tid; i < nwaves * E; i += blockDim.x)
+    for (int i = tid; i < 2 * E; i += NT)
+        pre[i] = 0;  // pre and post
+    for (int i = tid; i < nwaves * E; i += NT)
         cnt[i] = 0;
+    if (tid < 2)
+        misc[tid] = 0;
     __syncthreads();
 
-    // 1. histogram of every pair, and of the pairs before this block
+    // 1. histogram of every pair: whole batches of kHistBatch 16-byte loads
+    //    per thread (no bounds tests) are in flight before their atomics;
+    //    small batches only take the one-load loop after them
     int32_t invalid = 0;
+    const auto count = [&](int32_t e, int64_t q) {
+        if (e >= 0 && e < E)
+            atomicAdd((q < c0 ? pre : post) + e, 1);
+        else if (e != -1)
+            ++invalid;
+    };
+    const auto count4 = [&](const int4 &v, int64_t q) {
+        count(v.x, q);
+        count(v.y, q + 1);
+        count(v.z, q + 2);
+        count(v.w, q + 3);
+    };
     const bool vec_ok = ((uintptr_t)a.topk_idx & 15) == 0;  // 16-byte loads need 16-byte alignment
     const int64_t nvec = vec_ok ? a.P / 4 : 0;
     const int4 *v4 = reinterpret_cast<const int4 *>(a.topk_idx);
-#pragma unroll 4
-    for (int64_t i = tid; i < nvec; i += blockDim.x) {
-        const int4 q = v4[i];
-        const int32_t ee[4] = {q.x, q.y, q.z, q.w};
+    int64_t i = tid;
+    for (; i + (int64_t)(kHistBatch - 1) * NT < nvec; i += (int64_t)kHistBatch * NT) {
+        int4 v[kHistBatch];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int32_t e = ee[c];
-            if (e >= 0 && e < E)
-                atomicAdd(&hist[e], 1ull + (4 * i + c < c0 ? (1ull << 32) : 0ull));
-            else if (e != -1)
-                ++invalid;
-        }
+        for (int j = 0; j < kHistBatch; ++j)
+            v[j] = v4[i + (int64_t)j * NT];
+#pragma unroll
+        for (int j = 0; j < kHistBatch; ++j)
+            count4(v[j], 4 * (i + (int64_t)j * NT));
     }
-    for (int64_t q = 4 * nvec + tid; q < a.P; q += blockDim.x) {
-        const int32_t e = a.topk_idx[q];
-        if (e >= 0 && e < E)
-            atomicAdd(&hist[e], 1ull + (q < c0 ? (1ull << 32) : 0ull));
-        else if (e != -1)
-            ++invalid;
-    }
+    for (; i < nvec; i += NT)
+        count4(v4[i], 4 * i);
+    for (int64_t q = 4 * nvec + tid; q < a.P; q += NT)
+        count(a.topk_idx[q], q);
+    if (invalid != 0)
+        atomicAdd(&misc[0], invalid);
 
     // 2. rank of the own pair among equal experts in its run
     const bool routed = e_own >= 0 && e_own < E;
@@ -217,30 +266,34 @@ __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, in
     const int below = lanes_below(m);
     if (routed && below == 0)
         cnt[wave * E + e_own] = __popcll(m);
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        invalid += __shfl_xor(invalid, d);
-    if (lane == 0)
-        red[wave] = invalid;
     __syncthreads();
-    if (tid == 0)
-        for (int w = 1; w < nwaves; ++w)
-            invalid += red[w];
 
     // 3. totals; per-wave slot bases start at the pairs of earlier blocks
-    for (int e = tid; e < E; e += blockDim.x) {
-        const unsigned long long h = hist[e];
-        tot[e] = (int32_t)(uint32_t)h;
-        int32_t s = (int32_t)(h >> 32);
-        for (int w = 0; w < nwaves; ++w) {
-            const int32_t c = cnt[w * E + e];
-            cnt[w * E + e] = s;
-            s += c;
-        }
+    //    (all of an expert's wave counts are read before any is rewritten)
+    for (int e = tid; e < E; e += NT) {
+        const int32_t before = pre[e];
+        tot[e] = before + post[e];
+        int32_t c[kMaxBlockWaves];
+#pragma unroll
+        for (int w = 0; w < kMaxBlockWaves; ++w)
+            c[w] = 0;
+#pragma unroll
+        for (int w = 0; w < kMaxBlockWaves; ++w)
+            if (w < nwaves)
+                c[w] = cnt[w * E + e];
+        int32_t s = before;
+#pragma unroll
+        for (int w = 0; w < kMaxBlockWaves; ++w)
+            if (w < nwaves) {
+                cnt[w * E + e] = s;
+                s += c[w];
+            }
     }
     __syncthreads();
+    count_overflow<NT>(a, tot, &misc[1]);  // read after the barriers of step 4
 
     // 4. segment offsets, then the own pair's row and both maps
-    segment_offsets(a, tot, off, red);
+    segment_offsets<NT>(a, tot, off, red);
     if (own) {
         const int32_t row = routed ? row_of(a, off, e_own, cnt[wave * E + e_own] + below) : -1;
         a.h.pair_to_row[p] = row;
@@ -251,8 +304,8 @@ __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, in
     }
 
     // 5. rows that hold no pair; 6. counts and offsets, a slice per block
-    fill_unused_rows(a, tot, off);
-    publish(a, tot, off, red, invalid);
+    fill_unused_rows<NT>(a, tot, off);
+    publish<NT>(a, tot, off, misc[1], misc[0]);
 }
 
 // ---------------------------------------------------------------------------

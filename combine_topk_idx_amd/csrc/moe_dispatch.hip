@@ -48,16 +48,16 @@ __global__ __launch_bounds__(kBlockThreads) void dispatch_rows(DispatchArgs a)
 }
 
 template <int QUANT>
-__global__ __launch_bounds__(1024) void dispatch_fused(FusedArgs f)
+__global__ __launch_bounds__(kSingleThreads) void dispatch_fused(FusedArgs f)
 {
     extern __shared__ int32_t lds[];
-    __shared__ int32_t red[1024 / kWave];
+    __shared__ int32_t red[kMaxBlockWaves];
     const LayoutArgs &la = f.lay;
     const DispatchArgs &a = f.d;
     const RowPlan &pl = a.plan;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nwaves = blockDim.x / kWave;
+    constexpr int nwaves = kFusedWaves;
     int32_t *rows = lds + dev::single_layout_lds_words(la.E, nwaves);  // [tokens_per_block * K]
     const int t0 = blockIdx.x * f.tokens_per_block;
     const int t1 = min(a.T, t0 + f.tokens_per_block);

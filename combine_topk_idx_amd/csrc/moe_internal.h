@@ -12,11 +12,14 @@ namespace moe {
 constexpr int kWave = 64;             // CDNA wavefront width
 constexpr int kBlockThreads = 256;    // 4 waves per workgroup for the row kernels
 constexpr int kWavesPerBlock = kBlockThreads / kWave;
+constexpr int kMaxBlockWaves = 1024 / kWave;  // waves of the largest (1024-thread) blocks
+constexpr int kHistBatch = 8;                 // 16-byte id loads per thread in flight in a layout histogram
 constexpr int kQuantGroup = 128;      // 1x128 activation quantization group
 constexpr int kMaxTopk = 32;
 constexpr int kMaxExperts = 2048;     // layout keeps 7 int32 per expert in LDS
 constexpr int kLayoutMaxBlocks = 64;  // cap on layout blocks (columns of the histogram table)
 constexpr int64_t kSingleMaxPairs = 65536;  // largest batch the one-launch layout takes
+constexpr int kSingleMinBlocks = 16;         // one-launch blocks that share the unused-row fill
 
 // ---- layout ---------------------------------------------------------------
 
@@ -29,7 +32,7 @@ struct LayoutArgs {
     int32_t nbits;      // bits needed to tell experts apart (ballot match)
     int32_t rounds;     // runs of 64 pairs per wave
     int32_t chunk;      // pairs per block = waves * 64 * rounds
-    int32_t nblocks;    // blocks = ceil(P / chunk), >= 1, <= kLayoutMaxBlocks
+    int32_t nblocks;    // blocks = ceil(P / chunk) (one launch: at least kSingleMinBlocks), <= kLayoutMaxBlocks
     int32_t *ws;        // [E + 1][kLayoutMaxBlocks] per-block histograms (row E: invalid ids)
     int32_t *slots;     // [P] slot of each pair among its expert's pairs inside its block
     moe_handle_t h;
@@ -80,7 +83,9 @@ struct FusedPlan {
     RowPlan plan;
 };
 
+constexpr int kSingleThreads = 1024;   // block of the one-launch layout and of the fused dispatch
 constexpr int kFusedWaves = 16;         // waves per fused block (one block per compute unit)
+static_assert(kFusedWaves * kWave == kSingleThreads, "the fused block runs the one-launch layout");
 constexpr int kFusedMaxExperts = 512;   // keeps the block's LDS within 32 KiB
 
 struct CombineArgs {

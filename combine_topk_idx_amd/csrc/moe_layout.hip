@@ -36,6 +36,7 @@ namespace moe {
 
 namespace {
 
+using dev::count_overflow;
 using dev::fill_unused_rows;
 using dev::lanes_below;
 using dev::match_expert;
@@ -83,7 +84,7 @@ __device__ __forceinline__ void load_runs(int32_t (&v)[kTileRounds], const int32
 __global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
 {
     extern __shared__ int32_t cnt[];  // [WB][E]: per-wave counts, then per-wave slot bases
-    __shared__ int32_t red[1024 / kWave];
+    __shared__ int32_t red[kMaxBlockWaves];
     const int E = a.E;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -98,6 +99,8 @@ __global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
         load_runs(id, a.topk_idx, wr.w0, wr.w1, lane, -1);
     for (int i = tid; i < nwaves * E; i += blockDim.x)
         cnt[i] = 0;
+    if (tid == 0)
+        red[0] = 0;  // invalid ids of the block
     __syncthreads();
 
     // 1. rank of each pair among equal experts earlier in its wave's runs
@@ -126,28 +129,32 @@ __global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
             }
         }
     }
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        invalid += __shfl_xor(invalid, d);
-    if (lane == 0)
-        red[wave] = invalid;
+    if (invalid != 0)
+        atomicAdd(&red[0], invalid);  // rare
     __syncthreads();
 
-    // 2. per-wave slot bases inside the block; block histogram -> table column
+    // 2. per-wave slot bases inside the block (all of an expert's wave counts
+    //    read before any is rewritten); block histogram -> table column
     for (int e = tid; e < E; e += blockDim.x) {
+        int32_t c[kMaxBlockWaves];
+#pragma unroll
+        for (int w = 0; w < kMaxBlockWaves; ++w)
+            c[w] = 0;
+#pragma unroll
+        for (int w = 0; w < kMaxBlockWaves; ++w)
+            if (w < nwaves)
+                c[w] = cnt[w * E + e];
         int32_t s = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            const int32_t c = cnt[w * E + e];
-            cnt[w * E + e] = s;
-            s += c;
-        }
+#pragma unroll
+        for (int w = 0; w < kMaxBlockWaves; ++w)
+            if (w < nwaves) {
+                cnt[w * E + e] = s;
+                s += c[w];
+            }
         a.ws[(int64_t)e * kLayoutMaxBlocks + blk] = s;
     }
-    if (tid == 0) {
-        int32_t v = 0;
-        for (int w = 0; w < nwaves; ++w)
-            v += red[w];
-        a.ws[(int64_t)E * kLayoutMaxBlocks + blk] = v;
-    }
+    if (tid == 0)
+        a.ws[(int64_t)E * kLayoutMaxBlocks + blk] = red[0];
     __syncthreads();
 
     // 3. slot of each pair inside the block
@@ -191,7 +198,8 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
     int32_t *tot = lds;          // [E+1] pairs per expert, all blocks ([E]: invalid ids)
     int32_t *pre = tot + E + 1;  // [E+1] pairs per expert in earlier blocks
     int32_t *off = pre + E + 1;  // [E+1] segment starts
-    __shared__ int32_t red[1024 / kWave];
+    int32_t *over = off + E + 1; // [1] pairs the masked capacity drops
+    __shared__ int32_t red[kMaxBlockWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -215,6 +223,8 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
         tot[e] = 0;
         pre[e] = 0;
     }
+    if (tid == 0)
+        over[0] = 0;
     __syncthreads();
     const int cols = a.P > 0 ? a.nblocks : 0;
     const int nvec = (E + 1) * (kLayoutMaxBlocks / 4);
@@ -236,9 +246,10 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
             atomicAdd(&pre[e], p);
     }
     __syncthreads();
+    count_overflow<0>(a, tot, over);  // read after the barriers of step 2
 
     // 2. segment offsets
-    segment_offsets(a, tot, off, red);
+    segment_offsets<0>(a, tot, off, red);
 
     // 3. rows and both maps
     for (int64_t base = wr.w0; base < wr.w1; base += (int64_t)kTileRounds * kWave) {
@@ -262,16 +273,16 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
     }
 
     // 4. rows that hold no pair; 5. counts and offsets, a slice per block
-    fill_unused_rows(a, tot, off);
-    publish(a, tot, off, red, tot[E]);
+    fill_unused_rows<0>(a, tot, off);
+    publish<0>(a, tot, off, over[0], tot[E]);
 }
 
 // ---- schedule 1: one launch ---------------------------------------------------
 
-__global__ __launch_bounds__(1024) void layout_single(LayoutArgs a)
+__global__ __launch_bounds__(kSingleThreads) void layout_single(LayoutArgs a)
 {
     extern __shared__ int32_t lds[];
-    __shared__ int32_t red[1024 / kWave];
+    __shared__ int32_t red[kMaxBlockWaves];
     dev::single_layout_block(a, lds, red, nullptr);
 }
 
@@ -286,13 +297,17 @@ LayoutPlan layout_plan(int64_t P, int32_t E)
     LayoutPlan plan;
     plan.waves = layout_waves(E);
     plan.single = P <= kSingleMaxPairs && E <= 512;
+    if (plan.single)
+        plan.waves = kSingleThreads / kWave;  // the one-launch kernel is built for this block size
     const int64_t per_round = (int64_t)plan.waves * kWave;  // pairs per block per round
     int64_t rounds = (P + per_round * kLayoutMaxBlocks - 1) / (per_round * kLayoutMaxBlocks);
     if (rounds < 1 || plan.single)
         rounds = 1;
     plan.rounds = (int32_t)rounds;
     plan.chunk = (int32_t)(per_round * rounds);
-    const int64_t nb = (P + plan.chunk - 1) / plan.chunk;
+    int64_t nb = (P + plan.chunk - 1) / plan.chunk;
+    if (plan.single && nb < kSingleMinBlocks)
+        nb = kSingleMinBlocks;  // blocks past the last pair only fill unused rows and publish
     plan.nblocks = (int32_t)(nb < 1 ? 1 : nb);
     return plan;
 }
@@ -315,7 +330,7 @@ hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_
         const size_t lds = sizeof(int32_t) * (size_t)plan.waves * a.E;
         hipLaunchKernelGGL(layout_rank, grid, block, lds, stream, a);
     }
-    const size_t lds = sizeof(int32_t) * (size_t)(3 * a.E + 3);
+    const size_t lds = sizeof(int32_t) * (size_t)(3 * a.E + 4);
     hipLaunchKernelGGL(layout_index, grid, block, lds, stream, a);
     return hipGetLastError();
 }

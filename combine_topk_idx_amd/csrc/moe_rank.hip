@@ -116,12 +116,7 @@ __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(Ra
                 cnt += wtot[w][lane];
                 before += wbef[w][lane];
             }
-        int32_t incl = cnt;
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int32_t v = __shfl_up(incl, d);
-            if (lane >= d)
-                incl += v;
-        }
+        const int32_t incl = dev::wave_inclusive_sum(cnt);
         const int32_t off = incl - cnt;
         if (lane < R)
             base[lane] = off + before;
