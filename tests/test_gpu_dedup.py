@@ -22,7 +22,7 @@ import torch
 import combine_topk_idx_amd as M
 import oracle
 from combine_topk_idx_amd import workloads as W
-from test_gpu_parity import SENT, Guarded, _sentinel, make_cfg, oracle_scale_view, scale_cols, scale_guard
+from test_gpu_parity import SENT, Guarded, _sentinel, make_cfg, oracle_scale_view, random_case, scale_cols, scale_guard
 
 pytestmark = pytest.mark.gpu
 
@@ -230,6 +230,22 @@ def test_dedup_small(name, base, kw):
     inp = W.make_inputs(wl)
     y = W.expert_outputs(wl, inp)
     check(wl, inp.topk_idx, inp.topk_w, inp.x, y, make_cfg(wl))
+
+
+@pytest.mark.parametrize("i", range(16, 24))
+def test_dedup_random_configs(i):
+    """Seeded random configurations (the generator of the direct-path sweep,
+    other seeds): odd rank and expert counts, both layouts, every
+    quantization, T below max_tokens."""
+    c = random_case(i)
+    wl = W.Workload(f"random{i}", T=c["T"], H=c["H"], E=c["E"], K=c["K"], R=c["R"], layout=c["layout"],
+                    align=c["align"], capacity=c["capacity"], quant=c["quant"], routing=c["routing"],
+                    seed=c["seed"], expert_output="random")
+    _say(f"dedup random config {i}: {c}")
+    inp = W.make_inputs(wl)
+    cfg = make_cfg(wl, T_max=c["T_max"], num_cus=c["num_cus"])
+    y = W.expert_outputs(wl, inp, rows=M.moe_rows_capacity(cfg))
+    check(wl, inp.topk_idx, inp.topk_w, inp.x, y, cfg)
 
 
 def test_dedup_edge_routing():

@@ -275,6 +275,43 @@ def test_small_ragged(case, fused):
     check_parity(wl, idx, w, x, y, make_cfg(wl), f"small {case}", fused)
 
 
+# ---- seeded random configurations: every layout and quantization, odd expert
+# and rank counts, T below max_tokens, forced compute-unit counts (the fused
+# call's block count), with sizes kept small enough for the oracle
+
+def random_case(i):
+    rng = np.random.default_rng(9100 + i)
+    R = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    E = R * int(rng.integers(1, 48))
+    K = int(rng.integers(1, min(16, E) + 1))
+    quant = int(rng.choice([W.QUANT_NONE, W.QUANT_FP8_F32, W.QUANT_FP8_UE8M0, W.QUANT_MXFP8]))
+    H = 128 * int(rng.integers(1, 9)) if quant != W.QUANT_NONE else 8 * int(rng.integers(1, 129))
+    layout = int(rng.choice([W.LAYOUT_CONTIGUOUS, W.LAYOUT_MASKED]))
+    align = int(rng.choice([1, 2, 7, 32, 128]))
+    if E * align > 20000:
+        align = 7
+    T = int(rng.integers(1, 1500))
+    capacity = int(rng.integers(1, T * K // E + 9))
+    routing = "zipf" if rng.random() < 0.3 else "softmax"
+    return dict(T=T, H=H, E=E, K=K, R=R, layout=layout, align=align, capacity=capacity, quant=quant,
+                routing=routing, T_max=T + int(rng.integers(0, 100)),
+                num_cus=int(rng.choice([0, 1, 5, 64, 256])), seed=9100 + i)
+
+
+@pytest.mark.parametrize("fused", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("i", range(16))
+def test_random_configs(i, fused):
+    c = random_case(i)
+    _say(f"random config {i}: {c} fused={fused}")
+    wl = W.Workload(f"random{i}", T=c["T"], H=c["H"], E=c["E"], K=c["K"], R=c["R"], layout=c["layout"],
+                    align=c["align"], capacity=c["capacity"], quant=c["quant"], routing=c["routing"],
+                    seed=c["seed"])
+    cfg = make_cfg(wl, T_max=c["T_max"], num_cus=c["num_cus"])
+    inp = W.make_inputs(wl)
+    y = W.expert_outputs(wl, inp, rows=M.moe_rows_capacity(cfg))  # rows for max_tokens, not T
+    check_parity(wl, inp.topk_idx, inp.topk_w, inp.x, y, cfg, f"random config {i}", fused)
+
+
 def _edge_inputs(kind, T, H, E, K, rng):
     if kind == "one_expert":
         idx = np.zeros((T, K), np.int32)
