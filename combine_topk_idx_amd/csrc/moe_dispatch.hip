@@ -72,22 +72,34 @@ __global__ __launch_bounds__(kSingleThreads) void dispatch_fused(FusedArgs f)
         dev::load_item<QUANT>(r, a.x + (int64_t)t * a.H, it0, min(pl.iters_per_item, pl.n_iters - it0), a.H,
                               lane);
     }
-    dev::single_layout_block(la, lds, red, rows);
+    // items after the first ones are claimed from a block counter: the
+    // oldest waves win the memory arbitration and would otherwise finish
+    // early, leaving the block's last items to a few waves
+    __shared__ int32_t next_item;
+    if (threadIdx.x == 0)
+        next_item = nwaves;
+    dev::single_layout_block(la, lds, red, rows);  // its barriers publish next_item
     __syncthreads();
 
-    for (; item < nitems; item += nwaves) {
+    bool first = true;
+    while (item < nitems) {
+        int32_t claim = 0;
+        if (lane == 0)
+            claim = atomicAdd(&next_item, 1);  // in flight while this item moves
         const int t = t0 + item / pl.items_per_token;
         const int c = item % pl.items_per_token;
         const int it0 = c * pl.iters_per_item;
         const int n = min(pl.iters_per_item, pl.n_iters - it0);
-        if (item != wave)
+        if (!first)
             dev::load_item<QUANT>(r, a.x + (int64_t)t * a.H, it0, n, a.H, lane);
+        first = false;
         const int32_t myrow = lane < a.K ? rows[(t - t0) * a.K + lane] : -1;
         const uint64_t kept = __ballot(myrow >= 0);
         if (c == 0 && a.out_row_weight != nullptr && myrow >= 0)
             a.out_row_weight[myrow] = a.topk_w[(int64_t)t * a.K + lane];
         if (kept)
             dev::store_item<QUANT>(r, a, it0, n, lane, kept, myrow);
+        item = __builtin_amdgcn_readfirstlane(claim);
     }
 }
 
