@@ -155,7 +155,7 @@ def run_adapters(args, wl, cfg, d_idx, d_w, d_x, bufs, stream):
     copy_gbs = copy_ceiling(args.calib_copy_mib, dev, stream)
     return {"metric": "grouped-GEMM adapter GB/s per call (masked dispatch)", "value": gbs["repack_masked_to_contiguous"],
             "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup, "higher_is_better": True,
-            "vs_baseline": None, "data": "synthetic", "library_sha256": library_hash(),
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic", "library_sha256": library_hash(),
             "config": {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "capacity": C, "align": A,
                        "quant": QUANT_NAME[wl.quant]},
             "path": {"calls": [c for c, _ in calls], "per_call_ms_mean": ms, "algorithmic_bytes": ab,
@@ -231,7 +231,7 @@ def run_dedup(args, wl, cfg, d_idx, d_w, d_x, d_y, d_out, bufs, stream):
         "metric": "per-rank deduplicated dispatch+combine tokens/s (one GPU's local steps)",
         "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": wl.H, "experts": wl.E, "topk": wl.K,
                    "virtual_ranks": wl.R, "quant": QUANT_NAME[wl.quant]},
         "library_sha256": library_hash(),
@@ -720,11 +720,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, e4m3 dispatch, f32 accumulate" if wl.quant != W.QUANT_NONE
-                 else "bf16 in, bf16 dispatch, f32 accumulate",
+        "dtype": "f32",  # scales and the weighted sum are computed in fp32; the layout in int32
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": wl.H, "experts": wl.E,
                    "topk": wl.K, "virtual_ranks": wl.R,
+                   "io": ("bf16 tokens and expert outputs, " +
+                          ("e4m3 dispatched rows" if wl.quant != W.QUANT_NONE else "bf16 dispatched rows") +
+                          ", bf16 combined rows"),
                    "layout": "contiguous" if wl.layout == W.LAYOUT_CONTIGUOUS else "masked",
                    "align": wl.align, "capacity": wl.capacity, "quant": QUANT_NAME[wl.quant],
                    "num_cus": args.num_cus},
