@@ -185,13 +185,13 @@ __host__ __device__ inline size_t single_layout_lds_words(int32_t E, int waves)
 }
 
 // The whole layout for one block of kSingleThreads threads that needs nothing
-// from other blocks: the block owns pairs [blk*chunk, blk*chunk + chunk) (chunk <= 64 * waves, one
-// run of 64 pairs per wave).  It histograms ALL pairs itself (32-bit LDS
-// atomics, into `pre` for pairs before the block and `post` for the rest),
-// ranks its own pairs with a ballot match per run and the counts of earlier
-// waves, derives the segment offsets, writes both maps for its pairs, fills
-// its share of unused rows, and publishes its slice of the counts and offsets
-// (block 0 also the rank offsets and status).  Invalid ids and dropped pairs
+// from other blocks: the block owns pairs [blk*chunk, blk*chunk + chunk)
+// (chunk <= 64 * waves, one run of 64 pairs per wave).  It histograms ALL
+// pairs itself (32-bit LDS atomics, into `pre` for pairs before the block and
+// `post` for the rest), ranks its own pairs with a ballot match per run and
+// the counts of earlier waves, derives the segment offsets, writes both maps
+// for its pairs, fills its share of unused rows, and publishes its slice of
+// the counts and offsets (block 0 also the rank offsets and status).  Invalid ids and dropped pairs
 // are rare: lanes that have some add them into LDS counters with atomics.
 // `red` holds kMaxBlockWaves words.  When rows_out is given, rows_out[i]
 // receives the row of the block's pair i.

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(Ra
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nwaves = blockDim.x / kWave;
+    constexpr int nwaves = kRankLayoutWaves;  // the launch's block size (blockDim.x would be a load)
     const int R = a.R;
     const int t0 = blockIdx.x * a.tokens_per_block;
     const int t1 = min(a.T, t0 + a.tokens_per_block);
@@ -111,11 +111,13 @@ __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(Ra
     // 2. rank offsets (exclusive scan over ranks, one wave)
     if (wave == 0) {
         int32_t cnt = 0, before = 0;
-        if (lane < R)
-            for (int w = 0; w < nwaves; ++w) {
+        if (lane < R) {
+#pragma unroll
+            for (int w = 0; w < nwaves; ++w) {  // independent reads, all in flight
                 cnt += wtot[w][lane];
                 before += wbef[w][lane];
             }
+        }
         const int32_t incl = dev::wave_inclusive_sum(cnt);
         const int32_t off = incl - cnt;
         if (lane < R)
@@ -145,12 +147,21 @@ __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(Ra
     }
     __syncthreads();
     if ((int)threadIdx.x < R) {
+        // exclusive scan over the block's chunks, kScanBatch counts read before any is rewritten
+        constexpr int kScanBatch = 16;
         const int r = threadIdx.x;
         int32_t run = base[r];
-        for (int j = 0; j < nch; ++j) {
-            const int32_t c = chunk_base[j * R + r];
-            chunk_base[j * R + r] = run;
-            run += c;
+        for (int j0 = 0; j0 < nch; j0 += kScanBatch) {
+            int32_t c[kScanBatch];
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i)
+                c[i] = j0 + i < nch ? chunk_base[(j0 + i) * R + r] : 0;
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i)
+                if (j0 + i < nch) {
+                    chunk_base[(j0 + i) * R + r] = run;
+                    run += c[i];
+                }
         }
     }
     __syncthreads();
@@ -175,8 +186,9 @@ __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(Ra
     }
 
     // 5. rows past the last rank hold no token
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t q = total_rows + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < a.rows_cap; q += stride)
+    constexpr int kThreads = kRankLayoutWaves * kWave;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t q = total_rows + (int64_t)blockIdx.x * kThreads + threadIdx.x; q < a.rows_cap; q += stride)
         a.h.rank_row_to_token[q] = -1;
 }
 
