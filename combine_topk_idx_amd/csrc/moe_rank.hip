@@ -52,6 +52,22 @@ __device__ __forceinline__ uint32_t rank_mask(const RankLayoutArgs &a, int t)
     return m;
 }
 
+// Rank mask of a token from its KV 16-byte id vectors.
+template <int KV>
+__device__ __forceinline__ uint32_t rank_mask_of(const RankLayoutArgs &a, const int4 (&v)[KV])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < KV; ++i)
+        m |= rank_bit(a, v[i].x) | rank_bit(a, v[i].y) | rank_bit(a, v[i].z) | rank_bit(a, v[i].w);
+    return m;
+}
+
+// KV > 0: K = 4 * KV ids per token in 16-byte vectors, and phase 1 issues the
+// loads of all its chunks before any mask is formed (token indices are
+// clamped instead of branched on, so nothing splits the loads into separate
+// round trips).  KV = 0: any K, the token-by-token path.
+template <int KV>
 __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(RankLayoutArgs a)
 {
     extern __shared__ int32_t chunk_base[];  // [chunks of this block][R], then the block's token masks
@@ -73,13 +89,30 @@ __global__ __launch_bounds__(kRankLayoutWaves *kWave) void rank_layout_kernel(Ra
     //    of each wave accumulates rank r
     int32_t tot = 0, bef = 0;
     const int nchunks = (a.T + kWave - 1) / kWave;
-    constexpr int kPass = 4;  // chunks per wave whose loads are in flight together
+    constexpr int kPass = KV == 0 ? 4 : (KV <= 2 ? 4 : 2);  // chunks per wave whose loads are in flight together
     for (int c = wave; c < nchunks; c += kPass * nwaves) {
         uint32_t m[kPass];
+        if constexpr (KV > 0) {
+            int4 v[kPass][KV];
 #pragma unroll
-        for (int i = 0; i < kPass; ++i) {
-            const int t = (c + i * nwaves) * kWave + lane;
-            m[i] = t < a.T ? rank_mask(a, t) : 0u;
+            for (int i = 0; i < kPass; ++i) {
+                const int t = min((c + i * nwaves) * kWave + lane, a.T - 1);
+                const int4 *p = reinterpret_cast<const int4 *>(a.topk_idx + (int64_t)t * a.K);
+#pragma unroll
+                for (int j = 0; j < KV; ++j)
+                    v[i][j] = p[j];
+            }
+#pragma unroll
+            for (int i = 0; i < kPass; ++i) {
+                const int t = (c + i * nwaves) * kWave + lane;
+                m[i] = t < a.T ? rank_mask_of<KV>(a, v[i]) : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPass; ++i) {
+                const int t = (c + i * nwaves) * kWave + lane;
+                m[i] = t < a.T ? rank_mask(a, t) : 0u;
+            }
         }
         if (a.cache_masks) {
 #pragma unroll
@@ -284,7 +317,14 @@ hipError_t launch_rank_layout(const RankLayoutArgs &a, hipStream_t stream)
 {
     const size_t lds = sizeof(int32_t) * ((size_t)(a.tokens_per_block / kWave) * (size_t)a.R +
                                           (a.cache_masks ? (size_t)a.tokens_per_block : 0));
-    hipLaunchKernelGGL(rank_layout_kernel, dim3(a.nblocks), dim3(kRankLayoutWaves * kWave), lds, stream, a);
+    const dim3 grid(a.nblocks), block(kRankLayoutWaves * kWave);
+    const int kv = a.vec4 && a.T > 0 ? a.K / 4 : 0;
+    if (kv == 2)
+        hipLaunchKernelGGL(rank_layout_kernel<2>, grid, block, lds, stream, a);
+    else if (kv == 1)
+        hipLaunchKernelGGL(rank_layout_kernel<1>, grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL(rank_layout_kernel<0>, grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

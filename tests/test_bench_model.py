@@ -57,6 +57,8 @@ def test_short_kernel_names():
     assert bench.short_kernel("void moe::(anonymous namespace)::combine_kernel<true>(moe::CombineArgs)") \
         == "combine_kernel_partial"
     assert bench.short_kernel("moe::(anonymous namespace)::layout_single(moe::LayoutArgs)") == "layout_single"
+    assert bench.short_kernel("void moe::(anonymous namespace)::rank_layout_kernel<2>(moe::RankLayoutArgs)") \
+        == "rank_layout_kernel"
     assert bench.short_kernel("void moe::(anonymous namespace)::repack_kernel<true>(moe::RepackArgs)") \
         == "repack_to_contiguous"
 
