@@ -5,6 +5,7 @@
 // library allocates nothing and keeps no state besides a cached compute-unit
 // count per device.
 #include <limits.h>
+#include <string.h>
 
 #include <atomic>
 
@@ -687,7 +688,12 @@ moe_status_t moe_scales_mn_major(const moe_config_t *cfg, int32_t rows, const vo
 
 const char *moe_status_str(moe_status_t status)
 {
-    switch (status) {
+    // C callers may pass any int: read the bits as an int, since a C++ load of
+    // the enum outside its enumerators' range is undefined
+    static_assert(sizeof(int32_t) == sizeof(moe_status_t), "moe_status_t is 32 bits");
+    int32_t code;
+    memcpy(&code, &status, sizeof code);
+    switch (code) {
     case MOE_OK:
         return "MOE_OK";
     case MOE_ERR_INVALID_ARG:

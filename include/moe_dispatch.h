@@ -386,7 +386,8 @@ size_t moe_scale_words(const moe_config_t *cfg);
 moe_status_t moe_scales_mn_major(const moe_config_t *cfg, int32_t rows, const void *scale, void *scale_mn,
                                  void *stream);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code; any other value (any int)
+ * gives "MOE_ERR_UNKNOWN". */
 const char *moe_status_str(moe_status_t status);
 
 #ifdef __cplusplus

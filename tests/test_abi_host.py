@@ -70,6 +70,7 @@ def test_status_strings(lib):
     assert M.moe_status_str(2) == "MOE_ERR_CAPACITY"
     assert M.moe_status_str(4) == "MOE_ERR_HIP"
     assert M.moe_status_str(99) == "MOE_ERR_UNKNOWN"
+    assert M.moe_status_str(-1) == "MOE_ERR_UNKNOWN"   # any int from C, read without an enum load
 
 
 def test_size_queries(lib):
