@@ -10,7 +10,6 @@ import json
 import os
 
 import numpy as np
-import pytest
 import torch
 
 import oracle
