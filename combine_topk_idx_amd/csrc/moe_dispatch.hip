@@ -129,7 +129,27 @@ bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32
 {
     if (T <= 0 || E > kFusedMaxExperts || (int64_t)T * K > kSingleMaxPairs)
         return false;
-    int blocks = num_cus > 0 ? num_cus : device_cu_count();
+    int blocks = num_cus;
+    if (blocks <= 0) {
+        // By default a block per compute unit.  Large batches run their row
+        // phase faster on fewer compute units, one full block each over a
+        // longer token run: the phase is bound by the row stores, and at the
+        // DeepSeek-V3 prefill shape 7/16 of the compute units (power-of-two
+        // scales) or half of them (bf16 rows, fp32 scales, whose division
+        // needs more ALU) beat every compute unit by 4-6%.
+        const int cus = device_cu_count();
+        blocks = cus;
+        if (T >= kFusedLargeTokensPerCu * cus) {
+            const bool pow2_scales = quant == MOE_QUANT_FP8_UE8M0 || quant == MOE_QUANT_MXFP8;
+            blocks = pow2_scales ? cus * 7 / 16 : cus / 2;
+            const int per_block_max = kFusedWaves * kWave / K;  // one run of 64 pairs per wave
+            const int need = (T + per_block_max - 1) / per_block_max;
+            if (blocks < need)
+                blocks = need;
+            if (blocks < 1)
+                blocks = 1;
+        }
+    }
     if (blocks > T)
         blocks = T;
     const int tpb = (T + blocks - 1) / blocks;
