@@ -188,10 +188,14 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
  * row weights are those of moe_dispatch.
  *
  * For batches of at most 65536 pairs and at most 512 experts it is one
- * launch: one block per compute unit owns a run of tokens, issues the loads
- * of its token rows first and builds the layout for its pairs while they are
- * in flight.  Other batches run the layout and dispatch kernels back to back.
- * With num_cus > 0 the one-launch form uses that many blocks.
+ * launch: each block (at most one per compute unit) owns a run of tokens,
+ * issues the loads of its token rows first and builds the layout for its
+ * pairs while they are in flight.  Batches of at least 8 tokens per compute
+ * unit use 7/16 of the compute units (UE8M0 and MXFP8 scales) or half of
+ * them (bf16 rows, fp32 scales), whose row stores then run faster; smaller
+ * batches use a block per compute unit.  Other batches run the layout and
+ * dispatch kernels back to back.  With num_cus > 0 the one-launch form uses
+ * that many blocks.
  */
 moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
                                 const uint16_t *x, const float *topk_w, const moe_handle_t *handle,
