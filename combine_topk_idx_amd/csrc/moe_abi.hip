@@ -213,7 +213,8 @@ moe_status_t prepare_dispatch(const moe_config_t *cfg, int32_t num_tokens, const
     a.T = num_tokens;
     a.K = cfg->num_topk;
     a.H = cfg->hidden;
-    if (num_tokens > 0)
+    a.tokens_per_block = 0;
+    if (num_tokens > 0 && !runs_plan(num_tokens, cfg->hidden, cfg->quant, cfg->num_cus, a))
         a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus,
                                 kDispatchMinItemsPerToken)
                      : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus,
@@ -444,6 +445,10 @@ moe_status_t moe_dispatch_dedup(const moe_config_t *cfg, int32_t num_tokens, con
     a.T = num_tokens;
     a.K = cfg->num_ranks;
     a.H = cfg->hidden;
+    // all compute units: with about half as many rows written per token as a
+    // pair dispatch, the token-run form of runs_plan measured slower here
+    // (DeepSeek-V3 prefill 61 -> 110 us)
+    a.tokens_per_block = 0;
     a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus,
                             kDispatchMinItemsPerToken)
                  : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus,

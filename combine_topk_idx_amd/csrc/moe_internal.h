@@ -68,6 +68,7 @@ struct DispatchArgs {
     float *out_row_weight;
     int32_t T, K, H;
     RowPlan plan;
+    int32_t tokens_per_block = 0;  // > 0: blocks of kFusedWaves waves own token runs (dispatch_runs)
 };
 
 // One launch for layout + dispatch (small batches): block b owns tokens
@@ -182,6 +183,7 @@ RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item
                  int32_t num_cus, int32_t min_items_per_token = 1);
 hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream);
 bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32_t num_cus, FusedPlan &fp);
+bool runs_plan(int32_t T, int32_t H, int32_t quant, int32_t num_cus, DispatchArgs &a);
 hipError_t launch_dispatch_fused(const FusedArgs &f, int32_t quant, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream);
