@@ -699,6 +699,8 @@ def main():
 
     per_ms = {"layout+dispatch": float(np.mean(dispatch_ms)), "combine": float(np.mean(combine_ms))}
     per_med = {"layout+dispatch": float(np.median(dispatch_ms)), "combine": float(np.median(combine_ms))}
+    per_p10_p90 = {k: [float(np.percentile(v, 10)), float(np.percentile(v, 90))]
+                   for k, v in (("layout+dispatch", dispatch_ms), ("combine", combine_ms))}
 
     status = bufs.handle.status.cpu().numpy()
     n_kept = int(bufs.handle.recv_count.cpu().numpy().sum())
@@ -741,7 +743,8 @@ def main():
                            "moe_dispatch_layout + moe_dispatch + moe_combine")
                           + (", one HIP graph replay per step" if graph is not None else ""),
                  "algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
-                 "per_call_ms_mean": per_ms, "per_call_ms_median": per_med, "per_call_gbs": gbs,
+                 "per_call_ms_mean": per_ms, "per_call_ms_median": per_med,
+                 "per_call_ms_p10_p90": per_p10_p90, "per_call_gbs": gbs,
                  "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
                  "event_ms_per_step": ms_total / args.steps,
                  "host_enqueue_ms_per_step": enqueue_ms[0] if enqueue_ms else None, "kept_pairs": n_kept,
