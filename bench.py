@@ -311,6 +311,7 @@ def kernel_bytes(bench):
     algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"]}
     for q in QUANT_TEMPLATE.values():
         algo[f"dispatch_rows_{q}"] = ab["dispatch"]
+        algo[f"dispatch_runs_{q}"] = ab["dispatch"]
         algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
     return algo
 
