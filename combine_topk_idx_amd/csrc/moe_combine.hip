@@ -43,19 +43,23 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
-// Stores the bf16 of the sums and clears them.
+// Stores the bf16 of the sums and clears them; NT: non-temporal stores.
+template <bool NT>
 __device__ __forceinline__ void store_row(uint16_t *row, const int (&col)[kVecs], const bool (&active)[kVecs],
                                           float (&acc)[kVecs][8])
 {
 #pragma unroll
     for (int s = 0; s < kVecs; ++s) {
         if (active[s]) {
-            uint4 o;
-            o.x = pack_bf16(acc[s][0], acc[s][1]);
-            o.y = pack_bf16(acc[s][2], acc[s][3]);
-            o.z = pack_bf16(acc[s][4], acc[s][5]);
-            o.w = pack_bf16(acc[s][6], acc[s][7]);
-            *reinterpret_cast<uint4 *>(row + col[s]) = o;
+            u32x4 o;
+            o[0] = pack_bf16(acc[s][0], acc[s][1]);
+            o[1] = pack_bf16(acc[s][2], acc[s][3]);
+            o[2] = pack_bf16(acc[s][4], acc[s][5]);
+            o[3] = pack_bf16(acc[s][6], acc[s][7]);
+            if constexpr (NT)
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(row + col[s]));
+            else
+                *reinterpret_cast<u32x4 *>(row + col[s]) = o;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -78,7 +82,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const uint4
     }
 }
 
-template <bool PARTIAL>
+template <bool PARTIAL, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -172,14 +176,14 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
                                                                  __builtin_amdgcn_readlane(grp, jj);
                             if (last) {
                                 uint16_t *prow = a.out + (int64_t)__builtin_amdgcn_readlane(qrow, jj) * a.H;
-                                store_row(prow, col, active, acc);
+                                store_row<NT>(prow, col, active, acc);
                             }
                         }
                     }
                 }
             }
             if constexpr (!PARTIAL)
-                store_row(outp, col, active, acc);
+                store_row<NT>(outp, col, active, acc);
         }
     }
 }
@@ -188,13 +192,19 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    if (a.stream_out)
+        hipLaunchKernelGGL((combine_kernel<false, true>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<false, false>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    if (a.stream_out)
+        hipLaunchKernelGGL((combine_kernel<true, true>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<true, false>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
     return hipGetLastError();
 }
 

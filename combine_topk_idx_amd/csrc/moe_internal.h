@@ -101,6 +101,7 @@ struct CombineArgs {
     const int32_t *topk_idx;
     const int32_t *token_rank_row;
     int32_t E, R, L;
+    int32_t stream_out;          // non-temporal output stores (outputs larger than kCombineStreamOutBytes)
 };
 
 // ---- per-rank (deduplicated) exchange --------------------------------------
@@ -201,5 +202,9 @@ constexpr int kDispatchMinItemsPerToken = 8;     // about 1024 columns per item:
 constexpr int kCombineWidth = kWave * 16;        // two vectors of 8 bf16 per lane
 constexpr int kCombineMaxIters = 64;
 constexpr int kCombineMinItemsPerToken = 8;      // about 1024 columns per item: many short waves
+// Combine outputs larger than half of MI355X's 256 MB Infinity Cache cannot
+// stay in it; they are written non-temporally so that their dirty lines do not
+// have to be written back while later kernels stream through the cache.
+constexpr int64_t kCombineStreamOutBytes = (int64_t)128 << 20;
 
 }  // namespace moe

@@ -52,10 +52,11 @@ def test_dedup_bytes_deepseek_prefill():
 def test_short_kernel_names():
     assert bench.short_kernel("void moe::(anonymous namespace)::dispatch_rows<2>(moe::DispatchArgs)") \
         == "dispatch_rows_fp8_ue8m0"
-    assert bench.short_kernel("void moe::(anonymous namespace)::combine_kernel<false>(moe::CombineArgs)") \
-        == "combine_kernel"
-    assert bench.short_kernel("void moe::(anonymous namespace)::combine_kernel<true>(moe::CombineArgs)") \
-        == "combine_kernel_partial"
+    for nt in ("false", "true"):
+        assert bench.short_kernel(f"void moe::(anonymous namespace)::combine_kernel<false, {nt}>(moe::CombineArgs)") \
+            == "combine_kernel"
+        assert bench.short_kernel(f"void moe::(anonymous namespace)::combine_kernel<true, {nt}>(moe::CombineArgs)") \
+            == "combine_kernel_partial"
     assert bench.short_kernel("moe::(anonymous namespace)::layout_single(moe::LayoutArgs)") == "layout_single"
     assert bench.short_kernel("void moe::(anonymous namespace)::rank_layout_kernel<2>(moe::RankLayoutArgs)") \
         == "rank_layout_kernel"
