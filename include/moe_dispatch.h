@@ -215,6 +215,9 @@ moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, con
  * out[t,:] = bf16_RNE( sum over k ascending with row = pair_to_row[t*K+k] >= 0
  * of topk_w[t*K+k] * y[row,:] ), accumulated in fp32 from +0 with the product
  * and the sum each rounded to fp32.  A token with no kept pair gives +0.
+ * An out larger than 128 MiB is written with non-temporal stores (it cannot
+ * stay in the 256 MB Infinity Cache); a smaller one stays cacheable for the
+ * kernel that reads it next.
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_HIP.
  */
 moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *y,
