@@ -85,7 +85,7 @@ struct FusedPlan {
 };
 
 constexpr int kSingleThreads = 1024;   // block of the one-launch layout and of the fused dispatch
-constexpr int kFusedWaves = 16;         // waves per fused block (one block per compute unit)
+constexpr int kFusedWaves = 16;         // waves per fused or token-run block (at most one block per compute unit)
 static_assert(kFusedWaves * kWave == kSingleThreads, "the fused block runs the one-launch layout");
 constexpr int kFusedMaxExperts = 512;   // keeps the block's LDS within 32 KiB
 constexpr int kFusedLargeTokensPerCu = 8;  // from this many tokens per compute unit, fewer fused blocks
