@@ -541,6 +541,8 @@ def main():
     ap.add_argument("--align", type=int, default=128, help="segment alignment for --adapters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="scratch written before each of a few extra steps timed with cold caches (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of the plain device copy run after the timed region (copy "
                          "ceiling, and the counter calibration for --summarize)")
@@ -714,6 +716,32 @@ def main():
     sep_gbs = {k: ab[k] / (sep[k] * 1e-3) / 1e9 for k in ab}
     path_gbs = total_bytes / (ms_step * 1e-3) / 1e9
 
+    # cold caches: each of these steps follows an untimed read of a scratch
+    # buffer larger than L2 plus the 256 MB Infinity Cache, so nothing the step
+    # reads is cached when it starts (the timed steps above run back to back
+    # and move 1.65 GB each, six times the Infinity Cache).  The flush reads
+    # rather than writes: a written scratch would leave the cache full of dirty
+    # lines whose write-back the step would pay for.
+    cold = None
+    if args.flush_mib > 0:
+        scratch = torch.ones(args.flush_mib << 18, dtype=torch.int32, device=dev)
+        n_cold = min(args.steps, 30)
+        ev_c = [new_events(2) for _ in range(n_cold)]
+        torch.cuda.synchronize()
+        for i in range(n_cold):
+            flushed = scratch.sum()  # on the current stream, which the library calls use too
+            ev_c[i][0].record(stream)
+            layout_dispatch(stream)
+            combine(stream)
+            ev_c[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [a.elapsed_time(b) for a, b in ev_c]
+        assert int(flushed.item()) == scratch.numel()
+        cold = {"flush_mib": args.flush_mib, "flush": "read", "steps": n_cold,
+                "ms_per_step_median": float(np.median(cold_ms)),
+                "ms_per_step_p10_p90": [float(np.percentile(cold_ms, 10)), float(np.percentile(cold_ms, 90))]}
+        del scratch, flushed
+
     copy_gbs = copy_ceiling(args.calib_copy_mib, dev, stream)
 
     traffic = measured_traffic("combine_kernel", wl.name)
@@ -751,7 +779,7 @@ def main():
                  "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
                  "event_ms_per_step": ms_total / args.steps,
                  "host_enqueue_ms_per_step": enqueue_ms[0] if enqueue_ms else None, "kept_pairs": n_kept,
-                 "status": status.tolist(), "copy_ceiling_gbs": copy_gbs},
+                 "status": status.tolist(), "copy_ceiling_gbs": copy_gbs, "cold_caches": cold},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle), and the last step's outputs against it")

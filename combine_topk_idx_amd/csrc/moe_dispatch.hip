@@ -217,13 +217,16 @@ bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32
     if (blocks <= 0) {
         // By default a block per compute unit.  Large batches run their row
         // phase faster on fewer compute units, one full block each over a
-        // longer token run: the phase is bound by the row stores, and at the
-        // DeepSeek-V3 prefill shape 7/16 of the compute units (power-of-two
-        // scales) or half of them (bf16 rows, fp32 scales, whose division
-        // needs more ALU) beat every compute unit by 4-6%.
+        // longer token run, while the token rows are cached: the phase is
+        // then bound by the row stores, and at the DeepSeek-V3 prefill shape
+        // 7/16 of the compute units (power-of-two scales) or half of them
+        // (bf16 rows, fp32 scales, whose division needs more ALU) beat every
+        // compute unit by 4-6%.  Rows read from HBM need every compute unit's
+        // loads in flight (2x slower on 7/16 of them), so token rows too large
+        // to stay cached keep a block per compute unit.
         const int cus = device_cu_count();
         blocks = cus;
-        if (T >= kFusedLargeTokensPerCu * cus) {
+        if (T >= kFusedLargeTokensPerCu * cus && (int64_t)T * H * 2 <= kHalfInfinityCacheBytes) {
             blocks = large_batch_blocks(quant, cus);
             const int per_block_max = kFusedWaves * kWave / K;  // one run of 64 pairs per wave
             const int need = (T + per_block_max - 1) / per_block_max;
@@ -242,18 +245,19 @@ bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32
     return true;
 }
 
-// Separate dispatch of a large batch with power-of-two scales: token runs on
-// 7/16 of the compute units (dispatch_runs) move its rows faster than
-// dispatch_rows on all of them (DeepSeek-V3 prefill 93.4 -> 88.7 us).  With
-// fp32 scales the same change was slower on the skewed batches, and bf16 rows
-// showed no gain, so they keep dispatch_rows, as do smaller batches and an
-// explicit num_cus.
+// Separate dispatch of a large batch with power-of-two scales whose token
+// rows are likely cached: token runs on 7/16 of the compute units
+// (dispatch_runs) move its rows faster than dispatch_rows on all of them
+// (DeepSeek-V3 prefill 93.4 -> 88.7 us).  With fp32 scales the same change
+// was slower on the skewed batches, bf16 rows showed no gain, and rows read
+// from HBM need every compute unit's loads in flight (120 -> 193 us), so
+// those keep dispatch_rows, as do smaller batches and an explicit num_cus.
 bool runs_plan(int32_t T, int32_t H, int32_t quant, int32_t num_cus, DispatchArgs &a)
 {
     if (num_cus > 0 || !(quant == MOE_QUANT_FP8_UE8M0 || quant == MOE_QUANT_MXFP8))
         return false;
     const int cus = device_cu_count();
-    if (T < kFusedLargeTokensPerCu * cus)
+    if (T < kFusedLargeTokensPerCu * cus || (int64_t)T * H * 2 > kHalfInfinityCacheBytes)
         return false;
     int blocks = large_batch_blocks(quant, cus);
     if (blocks > T)

@@ -202,9 +202,13 @@ constexpr int kDispatchMinItemsPerToken = 8;     // about 1024 columns per item:
 constexpr int kCombineWidth = kWave * 16;        // two vectors of 8 bf16 per lane
 constexpr int kCombineMaxIters = 64;
 constexpr int kCombineMinItemsPerToken = 8;      // about 1024 columns per item: many short waves
-// Combine outputs larger than half of MI355X's 256 MB Infinity Cache cannot
-// stay in it; they are written non-temporally so that their dirty lines do not
-// have to be written back while later kernels stream through the cache.
-constexpr int64_t kCombineStreamOutBytes = (int64_t)128 << 20;
+// Half of MI355X's 256 MB Infinity Cache.  Combine outputs larger than this
+// cannot stay in it; they are written non-temporally so that their dirty lines
+// do not have to be written back while later kernels stream through the cache.
+// Token rows up to this size are likely still cached when dispatch reads them
+// (the kernels that produced and routed them ran just before), which the
+// fewer-compute-unit dispatch plans rely on.
+constexpr int64_t kHalfInfinityCacheBytes = (int64_t)128 << 20;
+constexpr int64_t kCombineStreamOutBytes = kHalfInfinityCacheBytes;
 
 }  // namespace moe

@@ -172,7 +172,10 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens,
  * the OCP format (max 448), round to nearest even, sign kept.  Each token is read and
  * quantized once and its bytes stored to all of its kept rows.  Rows that no
  * kept pair maps to (padding, empty masked slots, dropped pairs) are NOT
- * written, in out_x, out_scale and out_row_weight alike.
+ * written, in out_x, out_scale and out_row_weight alike.  UE8M0 and MXFP8
+ * batches of at least 8 tokens per compute unit whose x fits in half of the
+ * Infinity Cache run on 7/16 of the compute units, as moe_dispatch_fused
+ * does (same caveat for an evicted x; num_cus > 0 keeps every unit).
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_HIP.
  */
 moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x,
@@ -191,11 +194,15 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
  * launch: each block (at most one per compute unit) owns a run of tokens,
  * issues the loads of its token rows first and builds the layout for its
  * pairs while they are in flight.  Batches of at least 8 tokens per compute
- * unit use 7/16 of the compute units (UE8M0 and MXFP8 scales) or half of
- * them (bf16 rows, fp32 scales), whose row stores then run faster; smaller
- * batches use a block per compute unit.  Other batches run the layout and
- * dispatch kernels back to back.  With num_cus > 0 the one-launch form uses
- * that many blocks.
+ * unit whose token rows x fit in half of the 256 MB Infinity Cache use 7/16
+ * of the compute units (UE8M0 and MXFP8 scales) or half of them (bf16 rows,
+ * fp32 scales): their row stores run faster that way while x is cached, as it
+ * is when the kernels that produced and routed x ran just before.  If x has
+ * been evicted, this form is up to 2x slower than a block per compute unit;
+ * such callers should pass num_cus = the device's compute-unit count.  Other
+ * batches use a block per compute unit.  Batches beyond the one-launch limits
+ * run the layout and dispatch kernels back to back.  With num_cus > 0 the
+ * one-launch form uses that many blocks.
  */
 moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
                                 const uint16_t *x, const float *topk_w, const moe_handle_t *handle,
