@@ -145,8 +145,24 @@ def moe_status_str(code: int) -> str:
     return _load().moe_status_str(code).decode()
 
 
+# Size queries depend on the config's values only; per-call marshalling asks
+# for them on every call, so they are remembered per config value.
+_size_cache: dict = {}
+
+
+def _cached_size(fn: str, cfg: MoeConfig, *extra) -> int:
+    key = (fn, bytes(cfg)) + extra
+    v = _size_cache.get(key)
+    if v is None:
+        if len(_size_cache) > 4096:
+            _size_cache.clear()
+        v = int(getattr(_load(), fn)(ctypes.byref(cfg), *extra))
+        _size_cache[key] = v
+    return v
+
+
 def moe_rows_capacity(cfg: MoeConfig) -> int:
-    return int(_load().moe_rows_capacity(ctypes.byref(cfg)))
+    return _cached_size("moe_rows_capacity", cfg)
 
 
 def moe_workspace_bytes(cfg: MoeConfig) -> int:
@@ -158,7 +174,7 @@ def moe_config_check(cfg: MoeConfig) -> int:
 
 
 def moe_rank_rows_capacity(cfg: MoeConfig) -> int:
-    return int(_load().moe_rank_rows_capacity(ctypes.byref(cfg)))
+    return _cached_size("moe_rank_rows_capacity", cfg)
 
 
 # ---- marshalling helpers ----------------------------------------------------
@@ -348,6 +364,9 @@ class DedupBuffers:
         self.partial = torch.empty((n, H), dtype=torch.int16, device=device) if partial else None
 
 
+_ELEM_BYTES = {torch.float32: 4, torch.int32: 4, torch.uint8: 1}
+
+
 def _scale_layout(cfg):
     """(dtype, columns) of a row's scales: fp32 per 128 channels, packed UE8M0
     words (4 blocks each), or MX E8M0 bytes per 32 channels; None for bf16."""
@@ -368,7 +387,7 @@ def _scale_ptr(cfg, t, rows, name):
             raise ValueError(f"{name} must be None without FP8 quantization")
         return None
     dt, cols = lay
-    return _ptr(t, torch.empty(0, dtype=dt).element_size(), rows * cols, name)
+    return _ptr(t, _ELEM_BYTES[dt], rows * cols, name)
 
 
 def moe_rank_layout(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, rank_handle: RankHandle,
