@@ -194,8 +194,11 @@ __host__ __device__ inline size_t single_layout_lds_words(int32_t E, int waves)
 // the counts and offsets (block 0 also the rank offsets and status).  Invalid ids and dropped pairs
 // are rare: lanes that have some add them into LDS counters with atomics.
 // `red` holds kMaxBlockWaves words.  When rows_out is given, rows_out[i]
-// receives the row of the block's pair i.
-__device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, int32_t *red, int32_t *rows_out)
+// receives the row of the block's pair i.  With finish = false steps 5 and 6
+// are left to single_layout_finish, which the caller runs later (nothing in
+// the block reads what they write).
+__device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, int32_t *red, int32_t *rows_out,
+                                           bool finish = true)
 {
     constexpr int NT = kSingleThreads;
     const int E = a.E;
@@ -304,8 +307,22 @@ __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, in
     }
 
     // 5. rows that hold no pair; 6. counts and offsets, a slice per block
-    fill_unused_rows<NT>(a, tot, off);
-    publish<NT>(a, tot, off, misc[1], misc[0]);
+    if (finish) {
+        fill_unused_rows<NT>(a, tot, off);
+        publish<NT>(a, tot, off, misc[1], misc[0]);
+    }
+}
+
+// Steps 5 and 6 of single_layout_block(..., finish = false), from the totals,
+// offsets and rare counts it left in LDS.
+__device__ inline void single_layout_finish(const LayoutArgs &a, const int32_t *lds)
+{
+    constexpr int nwaves = kSingleThreads / kWave;
+    const int32_t *tot = lds + 2 * a.E;
+    const int32_t *off = tot + a.E;
+    const int32_t *misc = off + a.E + 1 + nwaves * a.E;
+    fill_unused_rows<kSingleThreads>(a, tot, off);
+    publish<kSingleThreads>(a, tot, off, misc[1], misc[0]);
 }
 
 // ---------------------------------------------------------------------------

@@ -118,7 +118,9 @@ __global__ __launch_bounds__(kSingleThreads) void dispatch_fused(FusedArgs f)
     __shared__ int32_t next_item;
     if (threadIdx.x == 0)
         next_item = nwaves;
-    dev::single_layout_block(la, lds, red, rows);  // its barriers publish next_item
+    // the unused-row fill and the published counts wait until after the rows:
+    // nothing here reads them, and waves without items do them meanwhile
+    dev::single_layout_block(la, lds, red, rows, false);  // its barriers publish next_item
     __syncthreads();
 
     bool first = true;
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(kSingleThreads) void dispatch_fused(FusedArgs f)
             dev::store_item<QUANT>(r, a, it0, n, lane, kept, myrow);
         item = __builtin_amdgcn_readfirstlane(claim);
     }
+    dev::single_layout_finish(la, lds);
 }
 
 }  // namespace
