@@ -255,6 +255,7 @@ SMALL = [
     (2600, 640, 64, 6, 4, W.LAYOUT_CONTIGUOUS, 32, 1, W.QUANT_MXFP8),     # fused: 7/16 of the CUs
     (2048, 16384, 32, 4, 4, W.LAYOUT_CONTIGUOUS, 8, 1, W.QUANT_FP8_UE8M0),  # token runs, two-iteration items
     (2100, 16384, 40, 3, 5, W.LAYOUT_MASKED, 1, 120, W.QUANT_MXFP8),     # token runs, MX, overflow
+    (8200, 8448, 64, 7, 8, W.LAYOUT_CONTIGUOUS, 16, 1, W.QUANT_FP8_UE8M0),  # x > 128 MiB: every CU, ragged row
     (9000, 512, 256, 8, 8, W.LAYOUT_CONTIGUOUS, 128, 1, W.QUANT_FP8_UE8M0),  # > 64 layout chunks
     (1, 2048, 128, 8, 8, W.LAYOUT_MASKED, 1, 128, W.QUANT_FP8_F32),       # T = 1
     (64, 8, 4, 4, 4, W.LAYOUT_CONTIGUOUS, 1, 1, W.QUANT_NONE),            # H = 8, E = R
