@@ -202,6 +202,7 @@ __device__ inline void single_layout_block(const LayoutArgs &a, int32_t *lds, in
 {
     constexpr int NT = kSingleThreads;
     const int E = a.E;
+    // LDS layout (single_layout_finish derives the same offsets)
     int32_t *pre = lds;          // [E] pairs before the block, then slot bases
     int32_t *post = pre + E;     // [E] pairs from the block on
     int32_t *tot = post + E;     // [E]
