@@ -313,7 +313,6 @@ def kernel_bytes(bench):
     algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"]}
     for q in QUANT_TEMPLATE.values():
         algo[f"dispatch_rows_{q}"] = ab["dispatch"]
-        algo[f"dispatch_runs_{q}"] = ab["dispatch"]
         algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
     return algo
 
@@ -458,14 +457,39 @@ def summarize(run_dir, calib_mib):
     print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
 
 
-CPU_BASELINE_SECONDS = 10.0
-CPU_BASELINE_MAX_PASSES = 5
+CPU_BASELINE_REPEATS = 3
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_threads():
+    """Threads for the all-cores leg: OMP_NUM_THREADS when set (the share of
+    the host this process is given), else every CPU the process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.strip().isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
-    """The CPU oracle (single thread, as it stands) on a bounded sample: the
-    first `max_tokens` tokens of the same batch, layout + dispatch + combine,
-    repeated until about CPU_BASELINE_SECONDS of work.
+    """The CPU oracle (as it stands) on a bounded sample: the first
+    `max_tokens` tokens of the same batch, layout + dispatch + combine, timed
+    on one thread and with the token loops of dispatch and combine split over
+    all host cores (OpenMP; the layout stays serial), median of
+    CPU_BASELINE_REPEATS passes each.
     When the sample is the whole batch and `gpu` holds the benchmark's final
     outputs (host copies), they are checked against the oracle's: layout and
     dispatched bytes bit for bit, combine within |g - o| <= 1e-2 |o| + 1e-5 S."""
@@ -481,17 +505,32 @@ def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
         ox, osc, _ = oracle.dispatch(x, h["pair_to_row"], wl.K, wl.quant, rows)
         return h, ox, osc, oracle.combine(y[:rows], w, h["pair_to_row"])
 
-    # passes until about CPU_BASELINE_SECONDS of work (at most CPU_BASELINE_MAX_PASSES)
-    t0 = time.perf_counter()
-    h, ox, osc, out = one_pass()
-    passes = 1
-    while time.perf_counter() - t0 < CPU_BASELINE_SECONDS and passes < CPU_BASELINE_MAX_PASSES:
-        one_pass()
-        passes += 1
-    dt = time.perf_counter() - t0
-    res = {"value": passes * T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-           "sample": f"first {T} of {wl.T} tokens of the same batch, {passes} layout+dispatch+combine "
-                     f"passes, single-threaded C oracle ({dt:.1f} s)"}
+    def leg(threads):
+        used = oracle.set_threads(threads)
+        times = []
+        try:
+            for _ in range(CPU_BASELINE_REPEATS):
+                t0 = time.perf_counter()
+                out = one_pass()
+                times.append(time.perf_counter() - t0)
+        finally:
+            oracle.set_threads(1)
+        return used, float(np.median(times)), out
+
+    n_all = cpu_threads()
+    all_used, all_s, _ = leg(n_all)
+    one_used, one_s, (h, ox, osc, out) = leg(1)
+    res = {"value": T / all_s, "unit": "tokens/s", "cores": all_used, "kind": "oracle",
+           "sample": f"first {T} of {wl.T} tokens of the same batch, layout + dispatch + combine, median of "
+                     f"{CPU_BASELINE_REPEATS} passes ({all_s:.2f} s each) with dispatch and combine split over "
+                     f"{all_used} OpenMP threads (layout serial)",
+           "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+           "gbs": None, "single_thread": {"value": T / one_s, "unit": "tokens/s", "cores": one_used,
+                                          "seconds_per_pass": one_s}}
+    n_kept = int((h["pair_to_row"] >= 0).sum())
+    ab = sum(algorithmic_bytes(sub, n_kept).values())
+    res["gbs"] = ab / all_s / 1e9
+    res["single_thread"]["gbs"] = ab / one_s / 1e9
     if gpu is not None and T == wl.T:
         check = {}
         check["layout_bit_exact"] = all(np.array_equal(gpu[k][:h[k].size], h[k]) for k in (
@@ -523,8 +562,8 @@ def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--num-cus", type=int, default=0)
     ap.add_argument("--separate", action="store_true",
@@ -542,7 +581,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--flush-mib", type=int, default=512,
-                    help="scratch written before each of a few extra steps timed with cold caches (0: skip)")
+                    help="scratch read before each timed step so that it starts with cold caches "
+                         "(0: time the headline steps back to back instead)")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of the plain device copy run after the timed region (copy "
                          "ceiling, and the counter calibration for --summarize)")
@@ -615,36 +655,15 @@ def main():
         torch.cuda.synchronize()
         return evs
 
-    def eager_steps(n):
-        """n steps with HIP events on the launch stream around each combine;
-        returns the combine and layout+dispatch times, the event time of all
-        steps and the wall time between two device synchronisations."""
-        beg, end = new_events(n), new_events(n)
-        t0, t1 = new_events(2)
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        t0.record(stream)
-        h0 = time.perf_counter()
-        for i in range(n):
-            layout_dispatch(stream)
-            beg[i].record(stream)
-            combine(stream)
-            end[i].record(stream)
-        t1.record(stream)
-        enqueue_ms.append((time.perf_counter() - h0) * 1e3 / n)
-        torch.cuda.synchronize()
-        wall_s = time.perf_counter() - w0
-        c_ms = [beg[i].elapsed_time(end[i]) for i in range(n)]
-        d_ms = [t0.elapsed_time(beg[0])] + [end[i - 1].elapsed_time(beg[i]) for i in range(1, n)]
-        return c_ms, d_ms, t0.elapsed_time(t1), wall_s
+    # cold caches: before each headline step an untimed read of a scratch
+    # buffer larger than L2 plus the 256 MB Infinity Cache evicts what the
+    # step reads.  The flush reads rather than writes: a written scratch would
+    # leave the cache full of dirty lines whose write-back the step would pay
+    # for, which is not the path's own cost.
+    scratch = torch.ones(max(args.flush_mib, 1) << 18, dtype=torch.int32, device=dev)
 
-    # warmup
-    log(f"[bench] warmup {args.warmup} steps ({'fused' if fused else 'separate'} dispatch"
-        f"{', graph replay' if args.graph else ''})")
-    for _ in range(args.warmup):
-        layout_dispatch(stream)
-        combine(stream)
-    torch.cuda.synchronize()
+    def flush():
+        return scratch.sum()  # on the current stream, which the library calls use too
 
     graph = None
     if args.graph:  # one step captured on a side stream, replayed on this one
@@ -661,33 +680,82 @@ def main():
             layout_dispatch(cap)
             combine(cap)
         torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
 
-    # timed region: K steps between two device synchronisations; eager steps
-    # carry HIP events on the launch stream around each combine (the dominant
-    # kernel); graph replays are timed as a whole
-    log(f"[bench] timing {args.steps} steps")
-    if graph is None:
-        combine_ms, dispatch_ms, ms_total, wall = eager_steps(args.steps)
-    else:
-        t0, t1 = new_events(2)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        t0.record(stream)
-        for _ in range(args.steps):
+    def run_step(st):
+        if graph is not None:
             graph.replay()
-        t1.record(stream)
+        else:
+            layout_dispatch(st)
+            combine(st)
+
+    def timed_steps(n, cold):
+        """n steps between two device synchronisations, each bracketed by HIP
+        events on the launch stream (and split at the dispatch/combine
+        boundary when eager); with `cold`, each step follows an untimed flush.
+        Returns per-step, per-dispatch and per-combine event times (ms) and the
+        wall time of the whole region (flushes included)."""
+        beg, mid, end = new_events(n), new_events(n), new_events(n)
+        flushed = None
         torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms_total = t0.elapsed_time(t1)
-    ms_step = wall * 1e3 / args.steps
-    if graph is not None:  # per-call times from eager steps after the timed region
-        combine_ms, dispatch_ms, _, _ = eager_steps(min(args.steps, 50))
+        w0 = time.perf_counter()
+        h0 = time.perf_counter()
+        for i in range(n):
+            if cold:
+                flushed = flush()
+            beg[i].record(stream)
+            if graph is not None:
+                graph.replay()
+            else:
+                layout_dispatch(stream)
+                mid[i].record(stream)
+                combine(stream)
+            end[i].record(stream)
+        if not cold:
+            enqueue_ms.append((time.perf_counter() - h0) * 1e3 / n)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - w0
+        if flushed is not None:
+            assert int(flushed.item()) == scratch.numel()
+        step = [beg[i].elapsed_time(end[i]) for i in range(n)]
+        if graph is not None:
+            return step, None, None, wall_s
+        return (step, [beg[i].elapsed_time(mid[i]) for i in range(n)],
+                [mid[i].elapsed_time(end[i]) for i in range(n)], wall_s)
+
+    # warmup
+    log(f"[bench] warmup {args.warmup} steps ({'fused' if fused else 'separate'} dispatch"
+        f"{', graph replay' if graph is not None else ''})")
+    for _ in range(args.warmup):
+        run_step(stream)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps between two device synchronisations.  The
+    # headline steps run with cold caches (an untimed flush before each);
+    # ms_per_step is the mean HIP-event time of the steps themselves.  With
+    # --flush-mib 0 the headline steps run back to back instead.
+    cold_headline = args.flush_mib > 0
+    log(f"[bench] timing {args.steps} steps ({'each after a cache flush' if cold_headline else 'back to back'})")
+    step_ms, dispatch_ms, combine_ms, wall = timed_steps(args.steps, cold_headline)
+    ms_step = float(np.mean(step_ms))
+    # secondary: the same number of steps back to back, timed by the wall
+    # clock between two synchronisations (the inputs stay cached from step to
+    # step: x is read by one dispatch and again by the next)
+    warm = None
+    if cold_headline:
+        log(f"[bench] timing {args.steps} steps back to back (warm caches)")
+        w_step, w_disp, w_comb, w_wall = timed_steps(args.steps, False)
+        warm = {"ms_per_step": w_wall * 1e3 / args.steps, "event_ms_per_step_mean": float(np.mean(w_step)),
+                "tokens_per_s": T / (w_wall / args.steps)}
+        if w_disp is not None:
+            warm["per_call_ms_mean"] = {"layout+dispatch": float(np.mean(w_disp)),
+                                        "combine": float(np.mean(w_comb))}
+    if dispatch_ms is None:  # graph replays: per-call times from eager steps after the timed region
+        saved, graph = graph, None
+        _, dispatch_ms, combine_ms, _ = timed_steps(min(args.steps, 50), cold_headline)
+        graph = saved
 
     # after the timed region: the same step as separate calls, each bracketed
-    # by events, for the per-call breakdown
+    # by events (back to back), for the per-call breakdown
     n_sep = min(args.steps, 50)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_sep)]
     for i in range(n_sep):
@@ -701,6 +769,11 @@ def main():
     torch.cuda.synchronize()
     sep = {k: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_sep)]))
            for j, k in enumerate(("layout", "dispatch", "combine"))}
+    # the headline step's own outputs for the oracle check below
+    if cold_headline:
+        flush()
+    run_step(stream)
+    torch.cuda.synchronize()
 
     per_ms = {"layout+dispatch": float(np.mean(dispatch_ms)), "combine": float(np.mean(combine_ms))}
     per_med = {"layout+dispatch": float(np.median(dispatch_ms)), "combine": float(np.median(combine_ms))}
@@ -715,32 +788,10 @@ def main():
            "combine": ab["combine"] / (per_ms["combine"] * 1e-3) / 1e9}
     sep_gbs = {k: ab[k] / (sep[k] * 1e-3) / 1e9 for k in ab}
     path_gbs = total_bytes / (ms_step * 1e-3) / 1e9
-
-    # cold caches: each of these steps follows an untimed read of a scratch
-    # buffer larger than L2 plus the 256 MB Infinity Cache, so nothing the step
-    # reads is cached when it starts (the timed steps above run back to back
-    # and move 1.65 GB each, six times the Infinity Cache).  The flush reads
-    # rather than writes: a written scratch would leave the cache full of dirty
-    # lines whose write-back the step would pay for.
-    cold = None
-    if args.flush_mib > 0:
-        scratch = torch.ones(args.flush_mib << 18, dtype=torch.int32, device=dev)
-        n_cold = min(args.steps, 30)
-        ev_c = [new_events(2) for _ in range(n_cold)]
-        torch.cuda.synchronize()
-        for i in range(n_cold):
-            flushed = scratch.sum()  # on the current stream, which the library calls use too
-            ev_c[i][0].record(stream)
-            layout_dispatch(stream)
-            combine(stream)
-            ev_c[i][1].record(stream)
-        torch.cuda.synchronize()
-        cold_ms = [a.elapsed_time(b) for a, b in ev_c]
-        assert int(flushed.item()) == scratch.numel()
-        cold = {"flush_mib": args.flush_mib, "flush": "read", "steps": n_cold,
-                "ms_per_step_median": float(np.median(cold_ms)),
-                "ms_per_step_p10_p90": [float(np.percentile(cold_ms, 10)), float(np.percentile(cold_ms, 90))]}
-        del scratch, flushed
+    if warm is not None:
+        warm["gbs"] = total_bytes / (warm["ms_per_step"] * 1e-3) / 1e9
+        warm["frac_of_peak"] = warm["gbs"] / HBM_PEAK_GBS
+    del scratch
 
     copy_gbs = copy_ceiling(args.calib_copy_mib, dev, stream)
 
@@ -765,21 +816,25 @@ def main():
                           ", bf16 combined rows"),
                    "layout": "contiguous" if wl.layout == W.LAYOUT_CONTIGUOUS else "masked",
                    "align": wl.align, "capacity": wl.capacity, "quant": QUANT_NAME[wl.quant],
-                   "num_cus": args.num_cus},
+                   "num_cus": args.num_cus,
+                   "caches": (f"cold: each timed step follows an untimed {args.flush_mib} MiB read"
+                              if cold_headline else "warm: steps back to back")},
         "library_sha256": library_hash(),
         "roofline": {"bound": "hbm", "kernel": "combine_kernel",
                      "achieved": gbs["combine"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs["combine"] / HBM_PEAK_GBS, "traffic": traffic},
         "path": {"calls": ("moe_dispatch_fused + moe_combine" if fused else
                            "moe_dispatch_layout + moe_dispatch + moe_combine")
-                          + (", one HIP graph replay per step" if graph is not None else ""),
+                          + (", one HIP graph replay per step" if args.graph else ""),
                  "algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
+                 "ms_per_step_median": float(np.median(step_ms)),
+                 "ms_per_step_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
+                 "timed_region_wall_s": wall,
                  "per_call_ms_mean": per_ms, "per_call_ms_median": per_med,
                  "per_call_ms_p10_p90": per_p10_p90, "per_call_gbs": gbs,
                  "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
-                 "event_ms_per_step": ms_total / args.steps,
                  "host_enqueue_ms_per_step": enqueue_ms[0] if enqueue_ms else None, "kept_pairs": n_kept,
-                 "status": status.tolist(), "copy_ceiling_gbs": copy_gbs, "cold_caches": cold},
+                 "status": status.tolist(), "copy_ceiling_gbs": copy_gbs, "warm_caches": warm},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle), and the last step's outputs against it")

@@ -213,8 +213,7 @@ moe_status_t prepare_dispatch(const moe_config_t *cfg, int32_t num_tokens, const
     a.T = num_tokens;
     a.K = cfg->num_topk;
     a.H = cfg->hidden;
-    a.tokens_per_block = 0;
-    if (num_tokens > 0 && !runs_plan(num_tokens, cfg->hidden, cfg->quant, cfg->num_cus, a))
+    if (num_tokens > 0)
         a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus,
                                 kDispatchMinItemsPerToken)
                      : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus,
@@ -338,6 +337,13 @@ moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, con
     if (st != MOE_OK)
         return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (num_tokens > 0 && fused_prefetch_plan(da, lp, cfg->num_cus, la)) {
+        // large batch: layout with x prefetched on the idle compute units, then the rows
+        hipError_t e = launch_layout(la, lp, s);
+        if (e == hipSuccess)
+            e = launch_dispatch(da, cfg->quant, s);
+        return from_hip(e);
+    }
     FusedPlan fp;
     if (fused_plan(num_tokens, cfg->num_topk, cfg->hidden, cfg->num_experts, cfg->quant, cfg->num_cus, fp)) {
         FusedArgs f;
@@ -446,10 +452,6 @@ moe_status_t moe_dispatch_dedup(const moe_config_t *cfg, int32_t num_tokens, con
     a.T = num_tokens;
     a.K = cfg->num_ranks;
     a.H = cfg->hidden;
-    // all compute units: with about half as many rows written per token as a
-    // pair dispatch, the token-run form of runs_plan measured slower here
-    // (DeepSeek-V3 prefill 61 -> 110 us)
-    a.tokens_per_block = 0;
     a.plan = fp8 ? row_plan(num_tokens, cfg->hidden, kDispatchFp8Width, kDispatchFp8MaxIters, cfg->num_cus,
                             kDispatchMinItemsPerToken)
                  : row_plan(num_tokens, cfg->hidden, kDispatchBf16Width, kDispatchBf16MaxIters, cfg->num_cus,

@@ -327,6 +327,52 @@ __device__ inline void single_layout_finish(const LayoutArgs &a, const int32_t *
 }
 
 // ---------------------------------------------------------------------------
+// Token rows: prefetch into the Infinity Cache
+// ---------------------------------------------------------------------------
+
+// Reads one dword of every kPrefetchSegment bytes of the token rows x [T, H]
+// in token order, so that the rows sit in the Infinity Cache -- the
+// memory-side cache every XCD reads HBM through -- when the row kernel that
+// follows loads them; the loaded values are discarded.  Run by `pf_blocks`
+// whole blocks of kSingleThreads threads; `pf_block` is this block's index
+// among them.  With the rows evicted, their HBM reads then happen while the
+// layout runs, instead of behind the row stores; with them cached, this is a
+// pass over them at cache bandwidth.
+__device__ inline void prefetch_rows(const uint16_t *x, int32_t T, int32_t H, int32_t pf_block, int32_t pf_blocks)
+{
+    constexpr int kWaves = kSingleThreads / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int32_t row_bytes = 2 * H;
+    const int32_t segs = (row_bytes + kPrefetchSegment - 1) / kPrefetchSegment;
+    const int32_t loads_per_row = (segs + kWave - 1) / kWave;
+    const int32_t units = T * loads_per_row;  // (token, load of 64 segments), token-major
+    const int32_t nw = pf_blocks * kWaves;
+    const char *base = reinterpret_cast<const char *>(x);
+    for (int32_t u0 = pf_block * kWaves + wave; u0 < units; u0 += nw * kPrefetchBatch) {
+        uint32_t v[kPrefetchBatch];
+#pragma unroll
+        for (int i = 0; i < kPrefetchBatch; ++i) {
+            v[i] = 0;
+            const int32_t u = u0 + i * nw;
+            if (u < units) {
+                const int32_t t = u / loads_per_row;
+                const int32_t seg = (u - t * loads_per_row) * kWave + lane;
+                // seg * 64 < row_bytes and both are multiples of 16: the dword is in the row
+                if (seg < segs)
+                    v[i] = *reinterpret_cast<const uint32_t *>(base + (int64_t)t * row_bytes +
+                                                               (int64_t)seg * kPrefetchSegment);
+            }
+        }
+        // the values are only consumed here, so the batch's loads are all in
+        // flight before the one wait for them
+#pragma unroll
+        for (int i = 0; i < kPrefetchBatch; ++i)
+            asm volatile("" ::"v"(v[i]));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Token rows: load, quantize, store
 // ---------------------------------------------------------------------------
 

@@ -47,46 +47,6 @@ __global__ __launch_bounds__(kBlockThreads) void dispatch_rows(DispatchArgs a)
     }
 }
 
-// The row phase of dispatch_fused over a layout already on the handle: block
-// b owns tokens [b * tokens_per_block, ...) and its waves claim the items of
-// those tokens from a block counter.  Large batches with power-of-two scales
-// use this on part of the compute units instead of dispatch_rows on all of
-// them (the row stores run faster; see runs_plan).
-template <int QUANT>
-__global__ __launch_bounds__(kSingleThreads) void dispatch_runs(DispatchArgs a)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const RowPlan &pl = a.plan;
-    const int64_t t0 = (int64_t)blockIdx.x * a.tokens_per_block;
-    const int64_t t1 = min((int64_t)a.T, t0 + a.tokens_per_block);
-    const int64_t nitems = (t1 - t0) * pl.items_per_token;
-    __shared__ int32_t next_item;
-    if (threadIdx.x == 0)
-        next_item = kFusedWaves;
-    __syncthreads();
-    int64_t item = wave;
-    while (item < nitems) {
-        int32_t claim = 0;
-        if (lane == 0)
-            claim = atomicAdd(&next_item, 1);  // in flight while this item moves
-        const int64_t t = t0 + item / pl.items_per_token;
-        const int c = (int)(item % pl.items_per_token);
-        const int it0 = c * pl.iters_per_item;
-        const int n = min(pl.iters_per_item, pl.n_iters - it0);
-        // the row loads and the token's rows are in flight together
-        dev::RowRegs<QUANT> r;
-        dev::load_item<QUANT>(r, a.x + t * a.H, it0, n, a.H, lane);
-        const int32_t myrow = lane < a.K ? a.pair_to_row[t * a.K + lane] : -1;
-        const uint64_t kept = __ballot(myrow >= 0);
-        if (c == 0 && a.out_row_weight != nullptr && myrow >= 0)
-            a.out_row_weight[myrow] = a.topk_w[t * a.K + lane];
-        if (kept)
-            dev::store_item<QUANT>(r, a, it0, n, lane, kept, myrow);
-        item = __builtin_amdgcn_readfirstlane(claim);
-    }
-}
-
 template <int QUANT>
 __global__ __launch_bounds__(kSingleThreads) void dispatch_fused(FusedArgs f)
 {
@@ -150,14 +110,6 @@ __global__ __launch_bounds__(kSingleThreads) void dispatch_fused(FusedArgs f)
 
 hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream)
 {
-    if (a.tokens_per_block > 0) {
-        const dim3 grid(a.plan.grid), block(kSingleThreads);
-        if (quant == MOE_QUANT_MXFP8)
-            hipLaunchKernelGGL(dispatch_runs<MOE_QUANT_MXFP8>, grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL(dispatch_runs<MOE_QUANT_FP8_UE8M0>, grid, block, 0, stream, a);
-        return hipGetLastError();
-    }
     const dim3 grid(a.plan.grid), block(kBlockThreads);
     switch (quant) {
     case MOE_QUANT_NONE:
@@ -178,18 +130,9 @@ hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t str
 
 namespace {
 
-// Blocks for a large batch spread as token runs: 7/16 of the compute units
-// for power-of-two scales, half of them otherwise (see fused_plan).
-int large_batch_blocks(int32_t quant, int cus)
-{
-    const bool pow2_scales = quant == MOE_QUANT_FP8_UE8M0 || quant == MOE_QUANT_MXFP8;
-    const int b = pow2_scales ? cus * 7 / 16 : cus / 2;
-    return b < 1 ? 1 : b;
-}
-
-// Items of a token-run plan (blocks of kFusedWaves waves, tpb tokens each):
-// short items, and enough of them to keep a block's waves busy when it owns
-// few tokens.
+// Items of a fused plan (blocks of kFusedWaves waves, tpb tokens each): short
+// items, and enough of them to keep a block's waves busy when it owns few
+// tokens.
 RowPlan token_run_items(int32_t T, int32_t H, int32_t quant, int32_t tpb, int32_t blocks)
 {
     const bool fp8 = quant != MOE_QUANT_NONE;
@@ -212,31 +155,13 @@ RowPlan token_run_items(int32_t T, int32_t H, int32_t quant, int32_t tpb, int32_
 
 }  // namespace
 
+// The one-launch fused kernel: a block per compute unit (or num_cus blocks),
+// each owning a run of tokens and at most one run of 64 pairs per wave.
 bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32_t num_cus, FusedPlan &fp)
 {
     if (T <= 0 || E > kFusedMaxExperts || (int64_t)T * K > kSingleMaxPairs)
         return false;
-    int blocks = num_cus;
-    if (blocks <= 0) {
-        // By default a block per compute unit.  Large batches run their row
-        // phase faster on fewer compute units, one full block each over a
-        // longer token run, while the token rows are cached: the phase is
-        // then bound by the row stores, and at the DeepSeek-V3 prefill shape
-        // 7/16 of the compute units (power-of-two scales) or half of them
-        // (bf16 rows, fp32 scales, whose division needs more ALU) beat every
-        // compute unit by 4-6%.  Rows read from HBM need every compute unit's
-        // loads in flight (2x slower on 7/16 of them), so token rows too large
-        // to stay cached keep a block per compute unit.
-        const int cus = device_cu_count();
-        blocks = cus;
-        if (T >= kFusedLargeTokensPerCu * cus && (int64_t)T * H * 2 <= kHalfInfinityCacheBytes) {
-            blocks = large_batch_blocks(quant, cus);
-            const int per_block_max = kFusedWaves * kWave / K;  // one run of 64 pairs per wave
-            const int need = (T + per_block_max - 1) / per_block_max;
-            if (blocks < need)
-                blocks = need;
-        }
-    }
+    int blocks = num_cus > 0 ? num_cus : device_cu_count();
     if (blocks > T)
         blocks = T;
     const int tpb = (T + blocks - 1) / blocks;
@@ -248,27 +173,29 @@ bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32
     return true;
 }
 
-// Separate dispatch of a large batch with power-of-two scales whose token
-// rows are likely cached: token runs on 7/16 of the compute units
-// (dispatch_runs) move its rows faster than dispatch_rows on all of them
-// (DeepSeek-V3 prefill 93.4 -> 88.7 us).  With fp32 scales the same change
-// was slower on the skewed batches, bf16 rows showed no gain, and rows read
-// from HBM need every compute unit's loads in flight (120 -> 193 us), so
-// those keep dispatch_rows, as do smaller batches and an explicit num_cus.
-bool runs_plan(int32_t T, int32_t H, int32_t quant, int32_t num_cus, DispatchArgs &a)
+// A fused call on a large batch (at least kPrefetchMinTokensPerCu tokens per
+// compute unit) whose token rows fit in half of the Infinity Cache runs as two
+// kernels: the one-launch layout, whose blocks leave most compute units idle,
+// with prefetch blocks on those units that bring x into the cache, then the
+// row kernel of the separate dispatch over every compute unit.  With x
+// evicted beforehand, the row kernel otherwise reads it from HBM behind its
+// own row stores (DeepSeek-V3 prefill: a one-launch fused call on a block per
+// compute unit 133 us, on 7/16 of them 191 us; this plan 119-120 us).  Sets
+// la's prefetch fields; false when the batch does not qualify or num_cus is
+// given.
+bool fused_prefetch_plan(const DispatchArgs &d, const LayoutPlan &lp, int32_t num_cus, LayoutArgs &la)
 {
-    if (num_cus > 0 || !(quant == MOE_QUANT_FP8_UE8M0 || quant == MOE_QUANT_MXFP8))
-        return false;
     const int cus = device_cu_count();
-    if (T < kFusedLargeTokensPerCu * cus || (int64_t)T * H * 2 > kHalfInfinityCacheBytes)
+    if (num_cus > 0 || !lp.single || d.T < kPrefetchMinTokensPerCu * cus ||
+        (int64_t)d.T * d.H * 2 > kHalfInfinityCacheBytes || la.nblocks >= cus)
         return false;
-    int blocks = large_batch_blocks(quant, cus);
-    if (blocks > T)
-        blocks = T;
-    const int tpb = (T + blocks - 1) / blocks;
-    blocks = (T + tpb - 1) / tpb;
-    a.plan = token_run_items(T, H, quant, tpb, blocks);
-    a.tokens_per_block = tpb;
+    const int64_t segs = ((int64_t)2 * d.H + kPrefetchSegment - 1) / kPrefetchSegment;
+    if ((int64_t)d.T * ((segs + kWave - 1) / kWave) > INT32_MAX / 2)
+        return false;
+    la.pf_x = d.x;
+    la.pf_T = d.T;
+    la.pf_H = d.H;
+    la.pf_blocks = cus - la.nblocks;
     return true;
 }
 

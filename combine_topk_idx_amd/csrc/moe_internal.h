@@ -36,6 +36,11 @@ struct LayoutArgs {
     int32_t *ws;        // [E + 1][kLayoutMaxBlocks] per-block histograms (row E: invalid ids)
     int32_t *slots;     // [P] slot of each pair among its expert's pairs inside its block
     moe_handle_t h;
+    // one-launch layout only: pf_blocks blocks after nblocks prefetch the
+    // token rows x [pf_T, pf_H] of the dispatch that follows into the
+    // Infinity Cache
+    const uint16_t *pf_x = nullptr;
+    int32_t pf_T = 0, pf_H = 0, pf_blocks = 0;
 };
 
 struct LayoutPlan {
@@ -68,7 +73,6 @@ struct DispatchArgs {
     float *out_row_weight;
     int32_t T, K, H;
     RowPlan plan;
-    int32_t tokens_per_block = 0;  // > 0: blocks of kFusedWaves waves own token runs (dispatch_runs)
 };
 
 // One launch for layout + dispatch (small batches): block b owns tokens
@@ -85,10 +89,12 @@ struct FusedPlan {
 };
 
 constexpr int kSingleThreads = 1024;   // block of the one-launch layout and of the fused dispatch
-constexpr int kFusedWaves = 16;         // waves per fused or token-run block (at most one block per compute unit)
+constexpr int kFusedWaves = 16;         // waves per fused block (at most one block per compute unit)
 static_assert(kFusedWaves * kWave == kSingleThreads, "the fused block runs the one-launch layout");
 constexpr int kFusedMaxExperts = 512;   // keeps the block's LDS within 32 KiB
-constexpr int kFusedLargeTokensPerCu = 8;  // from this many tokens per compute unit, fewer fused blocks
+constexpr int kPrefetchMinTokensPerCu = 8;  // from this many tokens per compute unit, a fused call prefetches x
+constexpr int kPrefetchSegment = 64;        // bytes of x each prefetch load stands for (one per segment)
+constexpr int kPrefetchBatch = 16;          // prefetch loads per lane in flight before the wave waits
 
 struct CombineArgs {
     const uint16_t *y;
@@ -184,7 +190,7 @@ RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item
                  int32_t num_cus, int32_t min_items_per_token = 1);
 hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream);
 bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32_t num_cus, FusedPlan &fp);
-bool runs_plan(int32_t T, int32_t H, int32_t quant, int32_t num_cus, DispatchArgs &a);
+bool fused_prefetch_plan(const DispatchArgs &d, const LayoutPlan &lp, int32_t num_cus, LayoutArgs &la);
 hipError_t launch_dispatch_fused(const FusedArgs &f, int32_t quant, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream);
@@ -205,9 +211,7 @@ constexpr int kCombineMinItemsPerToken = 8;      // about 1024 columns per item:
 // Half of MI355X's 256 MB Infinity Cache.  Combine outputs larger than this
 // cannot stay in it; they are written non-temporally so that their dirty lines
 // do not have to be written back while later kernels stream through the cache.
-// Token rows up to this size are likely still cached when dispatch reads them
-// (the kernels that produced and routed them ran just before), which the
-// fewer-compute-unit dispatch plans rely on.
+// Token rows up to this size are prefetched into it by a large fused dispatch.
 constexpr int64_t kHalfInfinityCacheBytes = (int64_t)128 << 20;
 constexpr int64_t kCombineStreamOutBytes = kHalfInfinityCacheBytes;
 

@@ -283,6 +283,10 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single(LayoutArgs a)
 {
     extern __shared__ int32_t lds[];
     __shared__ int32_t red[kMaxBlockWaves];
+    if ((int)blockIdx.x >= a.nblocks) {
+        dev::prefetch_rows(a.pf_x, a.pf_T, a.pf_H, blockIdx.x - a.nblocks, a.pf_blocks);
+        return;
+    }
     dev::single_layout_block(a, lds, red, nullptr);
 }
 
@@ -322,6 +326,7 @@ hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_
 {
     const dim3 grid(a.nblocks), block(plan.waves * kWave);
     if (plan.single) {
+        const dim3 grid(a.nblocks + a.pf_blocks);
         const size_t lds = sizeof(int32_t) * dev::single_layout_lds_words(a.E, plan.waves);
         hipLaunchKernelGGL(layout_single, grid, block, lds, stream, a);
         return hipGetLastError();

@@ -87,7 +87,10 @@ typedef struct {
     int32_t align;       /* contiguous: segment alignment in rows, >= 1 (ignored when masked) */
     int32_t capacity;    /* masked: rows per expert, >= 1 (ignored when contiguous) */
     int32_t quant;       /* moe_quant_t */
-    int32_t num_cus;     /* compute units the data kernels may occupy; 0 = all ([A2A] review: 0 = automatic) */
+    int32_t num_cus;     /* launch-shape override, not a reservation: 0 = automatic plans ([A2A] review:
+                            0 = automatic); > 0 = the row and combine grids are sized as if the device had
+                            this many compute units (at most 8 * num_cus workgroups of 256 threads) and the
+                            one-launch fused dispatch uses num_cus blocks; the layout kernels ignore it */
 } moe_config_t;
 
 /* The dispatch handle: caller-allocated int32 device arrays, written by
@@ -172,10 +175,9 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens,
  * the OCP format (max 448), round to nearest even, sign kept.  Each token is read and
  * quantized once and its bytes stored to all of its kept rows.  Rows that no
  * kept pair maps to (padding, empty masked slots, dropped pairs) are NOT
- * written, in out_x, out_scale and out_row_weight alike.  UE8M0 and MXFP8
- * batches of at least 8 tokens per compute unit whose x fits in half of the
- * Infinity Cache run on 7/16 of the compute units, as moe_dispatch_fused
- * does (same caveat for an evicted x; num_cus > 0 keeps every unit).
+ * written, in out_x, out_scale and out_row_weight alike.  The row kernel
+ * spreads short work items (a token's run of about 1024 channels) over every
+ * compute unit.
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_HIP.
  */
 moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x,
@@ -191,18 +193,16 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
  * row weights are those of moe_dispatch.
  *
  * For batches of at most 65536 pairs and at most 512 experts it is one
- * launch: each block (at most one per compute unit) owns a run of tokens,
- * issues the loads of its token rows first and builds the layout for its
- * pairs while they are in flight.  Batches of at least 8 tokens per compute
- * unit whose token rows x fit in half of the 256 MB Infinity Cache use 7/16
- * of the compute units (UE8M0 and MXFP8 scales) or half of them (bf16 rows,
- * fp32 scales): their row stores run faster that way while x is cached, as it
- * is when the kernels that produced and routed x ran just before.  If x has
- * been evicted, this form is up to 2x slower than a block per compute unit;
- * such callers should pass num_cus = the device's compute-unit count.  Other
- * batches use a block per compute unit.  Batches beyond the one-launch limits
- * run the layout and dispatch kernels back to back.  With num_cus > 0 the
- * one-launch form uses that many blocks.
+ * launch: each block (one per compute unit, or num_cus blocks) owns a run of
+ * tokens, issues the loads of its token rows first and builds the layout for
+ * its pairs while they are in flight.  Large batches (at least 8 tokens per
+ * compute unit) whose token rows x fit in half of the 256 MB Infinity Cache
+ * instead run two kernels, unless num_cus > 0: the one-launch layout, with
+ * the compute units it leaves idle reading x into the Infinity Cache
+ * meanwhile, then the row kernel of moe_dispatch over every compute unit.  So
+ * a call whose x was evicted from the caches reads it from HBM while the
+ * layout runs, not behind its own row stores.  Batches beyond the one-launch
+ * limits run the layout and dispatch kernels back to back.
  */
 moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
                                 const uint16_t *x, const float *topk_w, const moe_handle_t *handle,

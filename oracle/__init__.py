@@ -1,7 +1,8 @@
 """CPU oracle for MoE dispatch / combine -- TEST INFRASTRUCTURE ONLY.
 
 A ctypes front end over ``oracle/oracle.c`` (plain C, built with
-``gcc -O2 -ffp-contract=off``).  Only the test suite, the smoke entry point
+``gcc -O2 -ffp-contract=off -fopenmp``; one thread unless ``set_threads``
+asks for more).  Only the test suite, the smoke entry point
 and the benchmark's CPU-baseline leg may import this package; the HIP
 library never does, and this package never imports the HIP library.
 
@@ -34,7 +35,7 @@ _lib = None
 def build() -> str:
     """Compile oracle.c into liboracle.so (always recompiles)."""
     tmp = _LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fopenmp",
            "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
@@ -57,6 +58,11 @@ def _load():
     lib.oracle_dispatch.restype = None
     lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_combine.restype = None
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_get_threads.argtypes = []
+    lib.oracle_get_threads.restype = i32
+    lib.oracle_set_threads(1)  # one thread unless a caller asks for more
     lib.oracle_rank_layout.argtypes = [i32, i32, i32, i32, i64, P, P, P, P, P]
     lib.oracle_rank_layout.restype = ctypes.c_int
     lib.oracle_dispatch_dedup.argtypes = [i32, i32, i32, i32, P, P, P, P]
@@ -120,6 +126,14 @@ def dispatch_layout(topk_idx: np.ndarray, E: int, R: int, layout: int,
     if rc != 0:
         raise ValueError("rows needed exceed rows_capacity")
     return h
+
+
+def set_threads(n: int) -> int:
+    """Threads for the token loops of dispatch and combine (the layout is
+    serial); returns the count now in effect.  Results do not depend on it."""
+    lib = _load()
+    lib.oracle_set_threads(int(n))
+    return int(lib.oracle_get_threads())
 
 
 def dispatch(x: np.ndarray, pair_to_row: np.ndarray, K: int, quant: int, rows: int,

@@ -9,8 +9,10 @@
  * "bfloat16" with round-to-nearest-even, and the OCP 8-bit floating point
  * specification for E4M3 and E8M0), and its own layout arithmetic.
  *
- * Build: gcc -O2 -ffp-contract=off (no fast-math, SSE float on x86-64, so
- * every float operation below is one correctly rounded IEEE binary32 op).
+ * Build: gcc -O2 -ffp-contract=off -fopenmp (no fast-math, SSE float on
+ * x86-64, so every float operation below is one correctly rounded IEEE
+ * binary32 op).  OpenMP only splits the token loops of dispatch and combine
+ * across threads for the timing baseline; one thread is the default.
  *
  * What is computed, and the passages it follows (pages cited by title and
  * section):
@@ -56,6 +58,7 @@
  */
 #include <assert.h>
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -408,6 +411,12 @@ void oracle_dispatch(int32_t T, int32_t K, int32_t H, int32_t quant,
 {
     int32_t NB = H / ORACLE_BLOCK;
     int32_t NW = (NB + 3) / 4;
+    /* Tokens are independent (each writes only its own kept rows), so they
+     * may be split over threads; the bytes do not depend on the split.  The
+     * E4M3 value table is filled here, before any thread reads it. */
+    (void)e4m3_code_value(0);
+#pragma omp parallel
+    {
     uint8_t *q = NULL;
     float *s32 = NULL;
     uint32_t *w32 = NULL;
@@ -418,6 +427,7 @@ void oracle_dispatch(int32_t T, int32_t K, int32_t H, int32_t quant,
         w32 = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(4 * NW > 0 ? 4 * NW : 1));
         assert(q && s32 && w32);
     }
+#pragma omp for schedule(static)
     for (int32_t t = 0; t < T; t++) {
         const uint16_t *xt = x + (int64_t)t * H;
         int any = 0;
@@ -461,6 +471,7 @@ void oracle_dispatch(int32_t T, int32_t K, int32_t H, int32_t quant,
     free(q);
     free(s32);
     free(w32);
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -479,6 +490,8 @@ void oracle_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y,
                     const float *topk_w, const int32_t *pair_to_row,
                     uint16_t *out)
 {
+    /* tokens are independent: the same sums in the same order on any thread */
+#pragma omp parallel for schedule(static)
     for (int32_t t = 0; t < T; t++) {
         for (int32_t j = 0; j < H; j++) {
             float acc = 0.0f;
@@ -765,6 +778,18 @@ void oracle_scales_mn_major(int64_t rows, int32_t S, const uint32_t *in, uint32_
 /* ------------------------------------------------------------------------ */
 /* Array forms of the codecs, so the tests can sweep them in bulk           */
 /* ------------------------------------------------------------------------ */
+
+/* Threads for the token loops of oracle_dispatch and oracle_combine (OpenMP);
+ * the layout is serial.  Results do not depend on the count. */
+void oracle_set_threads(int32_t n)
+{
+    omp_set_num_threads(n < 1 ? 1 : n);
+}
+
+int32_t oracle_get_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 void oracle_bf16_rne_array(const float *in, uint16_t *out, int64_t n)
 {

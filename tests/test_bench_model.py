@@ -62,15 +62,15 @@ def test_short_kernel_names():
         == "rank_layout_kernel"
     assert bench.short_kernel("void moe::(anonymous namespace)::repack_kernel<true>(moe::RepackArgs)") \
         == "repack_to_contiguous"
-    assert bench.short_kernel("void moe::(anonymous namespace)::dispatch_runs<3>(moe::DispatchArgs)") \
-        == "dispatch_runs_mxfp8"
+    assert bench.short_kernel("void moe::(anonymous namespace)::dispatch_rows<3>(moe::DispatchArgs)") \
+        == "dispatch_rows_mxfp8"
 
 
 def test_kernel_bytes_cover_every_dispatch_kernel():
     ab = {"layout": 10, "dispatch": 100, "combine": 1000}
     algo = bench.kernel_bytes({"path": {"algorithmic_bytes": ab, "calls": "moe_dispatch_fused + moe_combine"}})
     for q in bench.QUANT_TEMPLATE.values():
-        assert algo[f"dispatch_rows_{q}"] == algo[f"dispatch_runs_{q}"] == 100
+        assert algo[f"dispatch_rows_{q}"] == 100
         assert algo[f"dispatch_fused_{q}"] == 110
     assert algo["combine_kernel"] == 1000 and algo["layout_single"] == 10
 
