@@ -99,6 +99,8 @@ def _load():
     lib.moe_config_check.restype = ctypes.c_int
     lib.moe_dispatch_layout.argtypes = [cfgp, i32, P, hp, P, sz, P]
     lib.moe_dispatch_layout.restype = ctypes.c_int
+    lib.moe_dispatch_layout_noalloc.argtypes = [cfgp, i32, P, hp, P]
+    lib.moe_dispatch_layout_noalloc.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [cfgp, i32, P, P, hp, P, P, P, P]
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_dispatch_fused.argtypes = [cfgp, i32, P, P, P, hp, P, sz, P, P, P, P]
@@ -263,6 +265,17 @@ def moe_dispatch_layout(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor,
     _check("moe_dispatch_layout", lib.moe_dispatch_layout(
         ctypes.byref(cfg), int(num_tokens), idx, ctypes.byref(handle.c), ws,
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_dispatch_layout_noalloc(cfg: MoeConfig, num_tokens: int, topk_idx: torch.Tensor, handle: Handle,
+                                stream=None) -> None:
+    """moe_dispatch_layout with the library's static per-GPU workspace (no
+    allocation; calls that overlap on one GPU race)."""
+    lib = _load()
+    K = cfg.num_topk
+    idx = _ptr(topk_idx, 4, num_tokens * K, "topk_idx") if num_tokens > 0 else None
+    _check("moe_dispatch_layout_noalloc", lib.moe_dispatch_layout_noalloc(
+        ctypes.byref(cfg), int(num_tokens), idx, ctypes.byref(handle.c), _stream(stream)))
 
 
 def _dispatch_ptrs(cfg, num_tokens, x, topk_w, out_x, out_scale, out_row_weight):

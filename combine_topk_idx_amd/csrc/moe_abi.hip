@@ -8,12 +8,52 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "moe_internal.h"
 
 namespace moe {
 
+// Workspace of moe_dispatch_layout_noalloc: one array per GPU, held until the
+// process ends, shared by every call on that GPU (calls that overlap on one
+// GPU race).  In host code `scratch` only names the array; its device
+// address comes from hipGetSymbolAddress, per device.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the scratch array on device `dev`, looked up once per
+// device with that device current; nullptr if the lookup fails.
+void *scratch_address(int dev)
+{
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex mu;
+    if (dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p != nullptr)
+        return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p != nullptr)
+        return p;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess)
+        return nullptr;
+    void *q = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (cur != dev)
+        (void)hipSetDevice(cur);
+    if (e != hipSuccess || q == nullptr)
+        return nullptr;
+    addr[dev].store(q, std::memory_order_release);
+    return q;
+}
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -308,6 +348,38 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens, co
     if (st != MOE_OK)
         return st;
     return from_hip(launch_layout(a, lp, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch_layout_noalloc(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
+                                         const moe_handle_t *handle, void *stream)
+{
+    // everything that needs no device first: the config, handle and token
+    // count, and the size of the workspace this call needs
+    moe_status_t st = check_config(cfg);
+    if (st != MOE_OK)
+        return st;
+    if ((st = check_handle(handle)) != MOE_OK)
+        return st;
+    if ((st = check_tokens(*cfg, num_tokens)) != MOE_OK)
+        return st;
+    if (num_tokens > 0 && (topk_idx == nullptr || !aligned(topk_idx, 4)))
+        return MOE_ERR_INVALID_ARG;
+    const size_t need = layout_table_bytes(cfg->num_experts) + sizeof(int32_t) * (size_t)num_tokens * cfg->num_topk;
+    if (need > kScratchBytes)
+        return MOE_ERR_CAPACITY;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if ((s != nullptr ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess)
+        return MOE_ERR_HIP;
+    void *ws = scratch_address(dev);
+    if (ws == nullptr)
+        return MOE_ERR_HIP;
+    LayoutArgs a;
+    LayoutPlan lp;
+    st = prepare_layout(cfg, num_tokens, topk_idx, handle, ws, kScratchBytes, a, lp);
+    if (st != MOE_OK)
+        return st;
+    return from_hip(launch_layout(a, lp, s));
 }
 
 moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *x, const float *topk_w,

@@ -149,6 +149,24 @@ moe_status_t moe_dispatch_layout(const moe_config_t *cfg, int32_t num_tokens,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moe_dispatch_layout without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of the library, 8 MiB on each GPU (held until the process ends, its address
+ * looked up once per GPU), so this call allocates nothing: it needs
+ * moe_workspace_bytes' table plus 4 bytes per pair, i.e. at most about 1.96M
+ * pairs (num_tokens * K) with 2048 experts.  Same arguments (minus the
+ * workspace), results and errors as moe_dispatch_layout; larger calls return
+ * MOE_ERR_CAPACITY before anything is enqueued.  Every call on a GPU shares
+ * its array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must not be issued.  The stream's device is used (the
+ * current device for a NULL stream).
+ */
+moe_status_t moe_dispatch_layout_noalloc(const moe_config_t *cfg, int32_t num_tokens,
+                                         const int32_t *topk_idx, const moe_handle_t *handle,
+                                         void *stream);
+
+/*
  * Dispatch: move token rows into the layout built by moe_dispatch_layout
  * (recv_x of [V2-PR] Motivation), quantizing them to FP8 on the way when
  * cfg.quant asks for it ([A2A] Implementation; [VLLM] commit: FP8

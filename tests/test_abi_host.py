@@ -34,7 +34,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"moe_rows_capacity", "moe_workspace_bytes", "moe_config_check",
-                          "moe_dispatch_layout", "moe_dispatch", "moe_dispatch_fused", "moe_combine",
+                          "moe_dispatch_layout", "moe_dispatch_layout_noalloc", "moe_dispatch", "moe_dispatch_fused",
+                          "moe_combine",
                           "moe_status_str", "moe_rank_rows_capacity", "moe_rank_layout",
                           "moe_dispatch_dedup", "moe_expand", "moe_combine_partial",
                           "moe_combine_reduce", "moe_row_expert", "moe_repack_rows_capacity",
@@ -138,6 +139,26 @@ def test_layout_argument_errors(lib):
     assert lib.moe_dispatch_layout(ctypes.byref(c), 4, FAKE, None, FAKE, 1 << 20, None) \
         == M.MOE_ERR_INVALID_ARG
     assert _layout(lib, _cfg(num_topk=40), 4) == M.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_layout_argument_errors(lib):
+    # every error below is found before the library touches a device
+    def call(cfg, T, idx=FAKE, h=None):
+        h = _handle() if h is None else h
+        return lib.moe_dispatch_layout_noalloc(ctypes.byref(cfg), T, idx, ctypes.byref(h), None)
+    c = _cfg()
+    assert call(c, 65) == M.MOE_ERR_CAPACITY           # num_tokens > max_tokens
+    assert call(c, -1) == M.MOE_ERR_INVALID_ARG
+    assert call(c, 4, idx=None) == M.MOE_ERR_INVALID_ARG
+    assert call(c, 4, idx=FAKE + 2) == M.MOE_ERR_INVALID_ARG
+    for f, _ in M.MoeHandle._fields_:
+        assert call(c, 4, h=_handle(**{f: None})) == M.MOE_ERR_INVALID_ARG, f
+    assert lib.moe_dispatch_layout_noalloc(ctypes.byref(c), 4, FAKE, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_layout_noalloc(None, 4, FAKE, ctypes.byref(_handle()), None) == M.MOE_ERR_INVALID_ARG
+    # the static workspace holds the 2048-expert table and 1,966,016 pair slots
+    big = _cfg(max_tokens=1 << 20, num_experts=2048, num_topk=2, num_ranks=2)
+    assert call(big, 1 << 20) == M.MOE_ERR_CAPACITY     # 2,097,152 pairs
+    assert call(big, 983009) == M.MOE_ERR_CAPACITY      # 1,966,018 pairs
 
 
 def _dispatch(lib, cfg, T, x=FAKE, w=None, out=FAKE, scale=None, rw=None, h=None):
