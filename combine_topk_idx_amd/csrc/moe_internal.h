@@ -91,7 +91,7 @@ struct FusedPlan {
 constexpr int kSingleThreads = 1024;   // block of the one-launch layout and of the fused dispatch
 constexpr int kFusedWaves = 16;         // waves per fused block (at most one block per compute unit)
 static_assert(kFusedWaves * kWave == kSingleThreads, "the fused block runs the one-launch layout");
-constexpr int kFusedMaxExperts = 512;   // keeps the block's LDS within 32 KiB
+constexpr int kFusedMaxExperts = 512;   // keeps the fused block's LDS within 44 KiB (80 E + 12 bytes + rows)
 constexpr int kPrefetchMinTokensPerCu = 8;  // from this many tokens per compute unit, a fused call prefetches x
 constexpr int kPrefetchSegment = 64;        // bytes of x each prefetch load stands for (one per segment)
 constexpr int kPrefetchBatch = 16;          // prefetch loads per lane in flight before the wave waits

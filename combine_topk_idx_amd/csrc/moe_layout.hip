@@ -16,10 +16,10 @@
 // No atomic decides an order, so the result is deterministic.  Two schedules
 // produce the same result:
 //   layout_single  (up to kSingleMaxPairs pairs, E <= 512) one launch, no
-//                  workspace: every block histograms ALL pairs itself (64-bit
-//                  LDS atomics: all pairs in the low word, pairs before the
-//                  block in the high word), so it needs nothing from other
-//                  blocks.  The redundant histogram costs about as much as a
+//                  workspace: every block histograms ALL pairs itself (32-bit
+//                  LDS atomics into two arrays, one for the pairs before the
+//                  block and one for the pairs from the block on), so it needs
+//                  nothing from other blocks.  The redundant histogram costs about as much as a
 //                  second launch would, and no table round trip is needed.
 //   layout_rank + layout_index  (larger batches) the rank kernel writes each
 //                  pair's slot and its block histogram (one column of an

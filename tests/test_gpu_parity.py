@@ -235,6 +235,33 @@ def test_workload_full_size(name, fused):
             assert np.array_equal(g[k], g2[k]), f"{name}: {k} not deterministic"
 
 
+# ---- scaled expert outputs at full size: oracle parity plus a closed form
+
+@pytest.mark.parametrize("name", ["deepseekv3_prefill_T8192", "deepseekv3_decode_T256", "qwen3moe_decode_T128"])
+def test_scaled_experts_full_size(name):
+    """Expert e returns bf16((e + 1) / 2 * x): combine must match the oracle
+    and, independently of it, the closed form x * sum over kept pairs of
+    w_k (e_k + 1) / 2 evaluated in float64.  All terms of a token share the
+    sign of x, so the relative error is at most the two bf16 roundings (y and
+    the output, 2^-8 each) plus the fp32 accumulation: 2^-7 + 2^-12 covers it."""
+    wl = W.WORKLOADS[name].replace(expert_output="scaled")
+    _say(f"full-size workload {name} with scaled expert outputs (fused)")
+    idx, w, x, y = inputs_for(wl)
+    cfg = make_cfg(wl)
+    g, o = check_parity(wl, idx, w, x, y, cfg, name + " scaled experts", fused=True)
+    T, K = idx.shape
+    p2r = o["pair_to_row"][:T * K].reshape(T, K)
+    kept = p2r >= 0
+    factor = np.where(kept, w.astype(np.float64) * (idx.astype(np.float64) + 1.0) * 0.5, 0.0).sum(axis=1)
+    ref = W.bf16_bits_to_f32(x).astype(np.float64) * factor[:, None]
+    got = W.bf16_bits_to_f32(g["out"]).astype(np.float64)
+    err = np.abs(got - ref)
+    tol = (2.0 ** -7 + 2.0 ** -12) * np.abs(ref)
+    assert np.all(err <= tol), f"{int((err > tol).sum())} elements off the closed form"
+    print(f"[ok] {name}: closed form, max relative error "
+          f"{float(np.max(err / np.maximum(np.abs(ref), 1e-300))):.3e}", flush=True)
+
+
 # ---- small cases spanning several tiles and ragged tails
 
 SMALL = [
