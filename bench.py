@@ -283,7 +283,8 @@ def short_kernel(name):
     stores, not a separate kernel); rank_layout_kernel<KV> (KV = id vectors per
     token, not a format) -> 'rank_layout_kernel'."""
     base = name.split("(moe::")[0].split("::")[-1]
-    named = {"repack_kernel<true>": "repack_to_contiguous", "repack_kernel<false>": "repack_to_masked"}
+    named = {"repack_kernel<true>": "repack_to_contiguous", "repack_kernel<false>": "repack_to_masked",
+             "layout_single<false>": "layout_single", "layout_single<true>": "layout_prefetch"}
     if base in named:
         return named[base]
     if base.startswith("combine_kernel<"):
@@ -310,7 +311,10 @@ def kernel_bytes(bench):
         for q in QUANT_TEMPLATE.values():
             algo[f"dispatch_rows_{q}"] = ab["dispatch_dedup"]
         return algo
-    algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"]}
+    # the large fused dispatch reads x into the Infinity Cache in its layout
+    # launch (layout_prefetch) and again from there in its row kernel; the
+    # algorithmic read of x belongs to the dispatch
+    algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"], "layout_prefetch": ab["layout"]}
     for q in QUANT_TEMPLATE.values():
         algo[f"dispatch_rows_{q}"] = ab["dispatch"]
         algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
@@ -339,24 +343,58 @@ def read_cmd(d, name):
         return "(command not recorded)"
 
 
+EXTRA_COUNTERS = ("VALUBusy", "VALUUtilization", "LDSBankConflict", "TCC_HIT_sum", "TCC_MISS_sum")
+
+
+def _counter_medians(run_dir, sub, names):
+    """{(kernel, grid): {counter: median per dispatch}} from a --pmc run
+    directory, or {} when the run is absent."""
+    d = os.path.join(run_dir, sub)
+    if not os.path.isdir(d):
+        return {}
+    vals = {}
+    for row in read_csv(find_file(d, "counter_collection.csv")):
+        if row["Counter_Name"] not in names:
+            continue
+        key = (row["Kernel_Name"], int(row["Grid_Size"]))
+        vals.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    return {k: {c: float(np.median(v)) for c, v in cs.items()} for k, cs in vals.items()}
+
+
+def _trace_stats(run_dir, sub):
+    """{kernel name: (calls, avg, min, max, stddev in us)} of a kernel-trace run, or {}."""
+    d = os.path.join(run_dir, sub)
+    if not os.path.isdir(d):
+        return {}
+    out = {}
+    for row in read_csv(find_file(d, "kernel_stats.csv")):
+        out[row["Name"]] = (row["Calls"],) + tuple(float(row[k]) / 1e3 for k in ("AverageNs", "MinNs", "MaxNs",
+                                                                                   "StdDev"))
+    return out
+
+
 def summarize(run_dir, calib_mib):
     """Write profiles/traffic.json and one Markdown summary per library
-    kernel from a run directory holding: prof_bench/ (kernel trace + stats),
-    pmc_FETCH_SIZE/ and pmc_WRITE_SIZE/ (one counter per run, with a
-    `calib_mib` MiB device copy in the same runs), bench.json (the benchmark
+    kernel from a run directory holding: prof_bench/ (kernel trace + stats of
+    back-to-back steps) and optionally prof_bench_cold/ (steps after a cache
+    flush), pmc_FETCH_SIZE/ and pmc_WRITE_SIZE/ (one counter per run, with a
+    `calib_mib` MiB device copy in the same runs), optionally pmc_extra/ and
+    pmc_extra_cold/ (VALU, LDS and L2 counters), bench.json (the benchmark
     line of the same build) and the *.cmd files naming the commands."""
     with open(os.path.join(run_dir, "bench.json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
     wl = W.WORKLOADS[bench["config"]["workload"]]
     adapters = "repack_masked_to_contiguous" in bench["path"]["algorithmic_bytes"]
     dedup = isinstance(bench["path"]["calls"], list) and not adapters
-    section = wl.name + (":dedup" if dedup else ":adapters" if adapters else "")
+    separate = isinstance(bench["path"]["calls"], str) and bench["path"]["calls"].startswith("moe_dispatch_layout")
+    section = wl.name + (":dedup" if dedup else ":adapters" if adapters else ":separate" if separate else "")
     built = bench.get("library_sha256")
     if built is None:
         raise SystemExit("bench.json names no library_sha256: rerun the benchmark with the current library")
     algo = kernel_bytes(bench)
 
-    stats = read_csv(find_file(os.path.join(run_dir, "prof_bench"), "kernel_stats.csv"))
+    stats = _trace_stats(run_dir, "prof_bench")
+    stats_cold = _trace_stats(run_dir, "prof_bench_cold")
     counters = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         for row in read_csv(find_file(os.path.join(run_dir, f"pmc_{c}"), "counter_collection.csv")):
@@ -364,6 +402,8 @@ def summarize(run_dir, calib_mib):
                 continue
             key = (row["Kernel_Name"], int(row["Grid_Size"]))
             counters.setdefault(c, {}).setdefault(key, []).append(float(row["Counter_Value"]))
+    extra = _counter_medians(run_dir, "pmc_extra", EXTRA_COUNTERS)
+    extra_cold = _counter_medians(run_dir, "pmc_extra_cold", EXTRA_COUNTERS)
     # calibration: the device copy is the copy kernel with the largest grid
     copies = {k: v for k, v in counters["FETCH_SIZE"].items() if "copyBuffer" in k[0]}
     ckey = max(copies, key=lambda k: k[1])
@@ -396,6 +436,9 @@ def summarize(run_dir, calib_mib):
                "algorithmic_bytes": algo.get(short)}
         if rec["algorithmic_bytes"]:
             rec["ratio"] = nbytes / rec["algorithmic_bytes"]
+        for tag, src in (("counters", extra), ("counters_cold", extra_cold)):
+            if (name, grid) in src:
+                rec[tag] = src[(name, grid)]
         traffic[section]["kernels"][short] = rec
         per_kernel[short] = rec
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -406,41 +449,40 @@ def summarize(run_dir, calib_mib):
     layout = "contiguous A=%d" % wl.align if wl.layout == W.LAYOUT_CONTIGUOUS else "masked C=%d" % wl.capacity
     title = (f"T={wl.T}, H={wl.H}, E={wl.E}, top-{wl.K}, {wl.R} virtual ranks, {layout}, "
              f"{QUANT_NAME[wl.quant]}")
-    trace_cmd = read_cmd(run_dir, "prof_bench")
-    pmc_cmds = [read_cmd(run_dir, "pmc_FETCH_SIZE"), read_cmd(run_dir, "pmc_WRITE_SIZE")]
     bench_cmd = read_cmd(run_dir, "bench")
     per_call = bench["path"]
-    for row in stats:
-        name = row["Name"]
-        if "moe::" not in name:
-            continue
+    names = {n for n in list(stats) + list(stats_cold) if "moe::" in n}
+    for name in sorted(names):
         short = short_kernel(name)
         if adapters and short not in algo:
             continue  # the dispatch that sets up the adapters run is profiled on its own
-        avg, mn, mx, sd = (float(row[k]) / 1e3 for k in ("AverageNs", "MinNs", "MaxNs", "StdDev"))
-        path_name = " (per-rank deduplicated path)" if dedup else " (grouped-GEMM adapters)" if adapters else ""
-        lines = [f"# {short} -- {wl.name}{path_name} ({title})", "",
-                 f"Kernel: `{name}`", "",
-                 "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
-                 "Command:", "", "    " + trace_cmd, "",
-                 "| Calls | Average | Min | Max | StdDev |", "|---|---|---|---|---|",
-                 f"| {row['Calls']} | {avg:.1f} us | {mn:.1f} us | {mx:.1f} us | {sd:.2f} us |", ""]
+        path_name = (" (per-rank deduplicated path)" if dedup else " (grouped-GEMM adapters)" if adapters else
+                     " (separate layout and dispatch calls)" if separate else "")
+        lines = [f"# {short} -- {wl.name}{path_name} ({title})", "", f"Kernel: `{name}`", ""]
         a = algo.get(short)
-        if a:
-            lines += [f"Algorithmic bytes per launch: {a:,} B -> {a / (avg * 1e3):,.0f} GB/s at the traced "
-                      f"average ({a / (avg * 1e3) / HBM_PEAK_GBS:.1%} of the 8 TB/s HBM peak).", ""]
-        lines += [f"Benchmark line of the same build (`{bench_cmd}`), HIP events on the launch stream:",
-                  (f"step {per_call['event_ms_per_step'] * 1e3:.1f} us, " if "event_ms_per_step" in per_call
-                   else "")
-                  + "per call "
+        for label, st, sub in (("back-to-back steps", stats, "prof_bench"),
+                               ("steps after a cache flush", stats_cold, "prof_bench_cold")):
+            if name not in st:
+                continue
+            calls, avg, mn, mx, sd = st[name]
+            lines += [f"## Kernel trace, {label} (rocprofv3 --kernel-trace --stats)", "", "Command:", "",
+                      "    " + read_cmd(run_dir, sub), "",
+                      "| Calls | Average | Min | Max | StdDev |", "|---|---|---|---|---|",
+                      f"| {calls} | {avg:.1f} us | {mn:.1f} us | {mx:.1f} us | {sd:.2f} us |", ""]
+            if a:
+                lines += [f"Algorithmic bytes per launch: {a:,} B -> {a / (avg * 1e3):,.0f} GB/s at the traced "
+                          f"average ({a / (avg * 1e3) / HBM_PEAK_GBS:.1%} of the 8 TB/s HBM peak).", ""]
+        sep = {k: v for k, v in per_call.get("separate_calls_ms_mean", {}).items() if v}
+        lines += [f"Benchmark line of the same build (`{bench_cmd}`), HIP events on the launch stream: "
+                  f"step {bench['ms_per_step'] * 1e3:.1f} us ({bench['config'].get('caches', '')}), per call "
                   + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["per_call_ms_mean"].items())
-                  + ("" if "separate_calls_ms_mean" not in per_call else "; separate calls " + ", ".join(
-                      f"{k} {v * 1e3:.1f} us" for k, v in per_call["separate_calls_ms_mean"].items()))
-                  + ".", ""]
+                  + ("" if not sep else "; separate calls (back to back) "
+                     + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in sep.items())) + ".", ""]
         rec = per_kernel.get(short)
         if rec:
-            lines += ["## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", ""]
-            lines += ["    " + c for c in pmc_cmds]
+            lines += ["## HBM traffic (rocprofv3 --pmc, one counter per run, back-to-back steps)", "",
+                      "Commands:", ""]
+            lines += ["    " + read_cmd(run_dir, f"pmc_{c}") for c in ("FETCH_SIZE", "WRITE_SIZE")]
             lines += ["", f"| Counter | KiB per dispatch (median of {rec['dispatches']}) | Scale | Bytes |",
                       "|---|---|---|---|",
                       f"| FETCH_SIZE | {rec['fetch_kib']:,.1f} | x{fscale:.4f} | {rec['fetch_kib'] * fscale * 1024:,.0f} |",
@@ -450,8 +492,23 @@ def summarize(run_dir, calib_mib):
                       f"Scale factors: the same runs copy {calib_mib} MiB device to device (kernel "
                       f"`{ckey[0]}`, grid {ckey[1]}); per {copy_kib:,.0f} KiB moved its FETCH_SIZE reads "
                       f"{cf:,.1f} KiB and its WRITE_SIZE {cw:,.1f} KiB, so FETCH_SIZE is multiplied by "
-                      f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f}.", ""]
-        fname = f"{short}_{wl.name}{'_dedup_path' if dedup else '_adapters' if adapters else ''}.md"
+                      f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f}. Both count L2 requests to the data "
+                      f"fabric: an Infinity Cache hit and an HBM access look the same to them.", ""]
+            for tag, label, sub in (("counters", "back-to-back steps", "pmc_extra"),
+                                    ("counters_cold", "steps after a cache flush", "pmc_extra_cold")):
+                cs = rec.get(tag)
+                if not cs:
+                    continue
+                hit, miss = cs.get("TCC_HIT_sum", 0.0), cs.get("TCC_MISS_sum", 0.0)
+                lines += [f"## VALU, LDS and L2 counters, {label} (rocprofv3 --pmc, median per dispatch)", "",
+                          "Command:", "", "    " + read_cmd(run_dir, sub), "",
+                          "| VALUBusy | VALUUtilization | LDSBankConflict | L2 hits | L2 misses | L2 hit rate |",
+                          "|---|---|---|---|---|---|",
+                          f"| {cs.get('VALUBusy', float('nan')):.1f}% | {cs.get('VALUUtilization', float('nan')):.1f}% "
+                          f"| {cs.get('LDSBankConflict', float('nan')):.2f}% | {hit:,.0f} | {miss:,.0f} | "
+                          f"{hit / max(hit + miss, 1.0):.1%} |", ""]
+        suffix = "_dedup_path" if dedup else "_adapters" if adapters else "_separate" if separate else ""
+        fname = f"{short}_{wl.name}{suffix}.md"
         with open(os.path.join(ROOT, "profiles", fname), "w") as f:
             f.write("\n".join(lines))
     print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
@@ -579,6 +636,10 @@ def main():
                     help="time the grouped-GEMM adapters on a masked workload instead")
     ap.add_argument("--align", type=int, default=128, help="segment alignment for --adapters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the secondary back-to-back steps (profiling runs of cold steps)")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-call breakdown after the timed region (profiling runs)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="scratch read before each timed step so that it starts with cold caches "
@@ -741,7 +802,7 @@ def main():
     # clock between two synchronisations (the inputs stay cached from step to
     # step: x is read by one dispatch and again by the next)
     warm = None
-    if cold_headline:
+    if cold_headline and not args.no_warm:
         log(f"[bench] timing {args.steps} steps back to back (warm caches)")
         w_step, w_disp, w_comb, w_wall = timed_steps(args.steps, False)
         warm = {"ms_per_step": w_wall * 1e3 / args.steps, "event_ms_per_step_mean": float(np.mean(w_step)),
@@ -756,7 +817,7 @@ def main():
 
     # after the timed region: the same step as separate calls, each bracketed
     # by events (back to back), for the per-call breakdown
-    n_sep = min(args.steps, 50)
+    n_sep = 0 if args.no_breakdown else min(args.steps, 50)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_sep)]
     for i in range(n_sep):
         ev[i][0].record(stream)
@@ -767,7 +828,7 @@ def main():
         combine(stream)
         ev[i][3].record(stream)
     torch.cuda.synchronize()
-    sep = {k: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_sep)]))
+    sep = {k: (float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_sep)])) if n_sep else None)
            for j, k in enumerate(("layout", "dispatch", "combine"))}
     # the headline step's own outputs for the oracle check below
     if cold_headline:
@@ -786,7 +847,7 @@ def main():
     total_bytes = sum(ab.values())
     gbs = {"layout+dispatch": (ab["layout"] + ab["dispatch"]) / (per_ms["layout+dispatch"] * 1e-3) / 1e9,
            "combine": ab["combine"] / (per_ms["combine"] * 1e-3) / 1e9}
-    sep_gbs = {k: ab[k] / (sep[k] * 1e-3) / 1e9 for k in ab}
+    sep_gbs = {k: ab[k] / (sep[k] * 1e-3) / 1e9 for k in ab if sep[k]}
     path_gbs = total_bytes / (ms_step * 1e-3) / 1e9
     if warm is not None:
         warm["gbs"] = total_bytes / (warm["ms_per_step"] * 1e-3) / 1e9

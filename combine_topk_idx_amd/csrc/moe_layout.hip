@@ -279,11 +279,14 @@ __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
 
 // ---- schedule 1: one launch ---------------------------------------------------
 
+// PREFETCH: blocks after a.nblocks bring the token rows of the dispatch that
+// follows into the Infinity Cache instead (the large fused dispatch).
+template <bool PREFETCH>
 __global__ __launch_bounds__(kSingleThreads) void layout_single(LayoutArgs a)
 {
     extern __shared__ int32_t lds[];
     __shared__ int32_t red[kMaxBlockWaves];
-    if ((int)blockIdx.x >= a.nblocks) {
+    if (PREFETCH && (int)blockIdx.x >= a.nblocks) {
         dev::prefetch_rows(a.pf_x, a.pf_T, a.pf_H, blockIdx.x - a.nblocks, a.pf_blocks);
         return;
     }
@@ -326,9 +329,11 @@ hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_
 {
     const dim3 grid(a.nblocks), block(plan.waves * kWave);
     if (plan.single) {
-        const dim3 grid(a.nblocks + a.pf_blocks);
         const size_t lds = sizeof(int32_t) * dev::single_layout_lds_words(a.E, plan.waves);
-        hipLaunchKernelGGL(layout_single, grid, block, lds, stream, a);
+        if (a.pf_blocks > 0)
+            hipLaunchKernelGGL(layout_single<true>, dim3(a.nblocks + a.pf_blocks), block, lds, stream, a);
+        else
+            hipLaunchKernelGGL(layout_single<false>, grid, block, lds, stream, a);
         return hipGetLastError();
     }
     if (a.P > 0) {
