@@ -626,9 +626,11 @@ def main():
     ap.add_argument("--separate", action="store_true",
                     help="time layout and dispatch as two calls instead of the fused call")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph and time graph replays (launch-bound "
+                    help="capture steps in a HIP graph and time graph replays (launch-bound "
                          "decode batches); per-call times then come from the eager calls after "
                          "the timed region")
+    ap.add_argument("--graph-steps", type=int, default=1,
+                    help="steps captured in one graph (--graph); --steps counts steps, not replays")
     ap.add_argument("--dedup", action="store_true",
                     help="time the per-rank deduplicated path instead (rank layout, dedup dispatch, "
                          "expansion, partial combine, reduction)")
@@ -654,6 +656,8 @@ def main():
         summarize(args.summarize, args.calib_copy_mib)
         return
 
+    if args.graph_steps < 1 or (args.graph_steps > 1 and not args.graph):
+        raise SystemExit("--graph-steps needs --graph and a count >= 1")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(destination ranks are virtual partitions of one device's buffers). "
@@ -738,8 +742,9 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             cap = torch.cuda.current_stream()
-            layout_dispatch(cap)
-            combine(cap)
+            for _ in range(args.graph_steps):
+                layout_dispatch(cap)
+                combine(cap)
         torch.cuda.synchronize()
 
     def run_step(st):
@@ -755,6 +760,8 @@ def main():
         boundary when eager); with `cold`, each step follows an untimed flush.
         Returns per-step, per-dispatch and per-combine event times (ms) and the
         wall time of the whole region (flushes included)."""
+        per = args.graph_steps if graph is not None else 1  # steps per replay
+        n = -(-n // per)
         beg, mid, end = new_events(n), new_events(n), new_events(n)
         flushed = None
         torch.cuda.synchronize()
@@ -763,13 +770,18 @@ def main():
         for i in range(n):
             if cold:
                 flushed = flush()
-            beg[i].record(stream)
             if graph is not None:
+                # back to back, replays carry no events of their own
+                if cold or i == 0:
+                    beg[i].record(stream)
                 graph.replay()
-            else:
-                layout_dispatch(stream)
-                mid[i].record(stream)
-                combine(stream)
+                if cold or i == n - 1:
+                    end[i].record(stream)
+                continue
+            beg[i].record(stream)
+            layout_dispatch(stream)
+            mid[i].record(stream)
+            combine(stream)
             end[i].record(stream)
         if not cold:
             enqueue_ms.append((time.perf_counter() - h0) * 1e3 / n)
@@ -777,7 +789,10 @@ def main():
         wall_s = time.perf_counter() - w0
         if flushed is not None:
             assert int(flushed.item()) == scratch.numel()
-        step = [beg[i].elapsed_time(end[i]) for i in range(n)]
+        if cold:
+            step = [beg[i].elapsed_time(end[i]) / per for i in range(n)]
+        else:  # back to back: the mean step is the span of all steps over their number
+            step = [beg[0].elapsed_time(end[n - 1]) / (n * per)] * n
         if graph is not None:
             return step, None, None, wall_s
         return (step, [beg[i].elapsed_time(mid[i]) for i in range(n)],
@@ -805,8 +820,8 @@ def main():
     if cold_headline and not args.no_warm:
         log(f"[bench] timing {args.steps} steps back to back (warm caches)")
         w_step, w_disp, w_comb, w_wall = timed_steps(args.steps, False)
-        warm = {"ms_per_step": w_wall * 1e3 / args.steps, "event_ms_per_step_mean": float(np.mean(w_step)),
-                "tokens_per_s": T / (w_wall / args.steps)}
+        w_ms = float(np.mean(w_step))  # span of the back-to-back steps over their number (HIP events)
+        warm = {"ms_per_step": w_ms, "wall_ms_per_step": w_wall * 1e3 / args.steps, "tokens_per_s": T / (w_ms * 1e-3)}
         if w_disp is not None:
             warm["per_call_ms_mean"] = {"layout+dispatch": float(np.mean(w_disp)),
                                         "combine": float(np.mean(w_comb))}
@@ -886,7 +901,7 @@ def main():
                      "frac": gbs["combine"] / HBM_PEAK_GBS, "traffic": traffic},
         "path": {"calls": ("moe_dispatch_fused + moe_combine" if fused else
                            "moe_dispatch_layout + moe_dispatch + moe_combine")
-                          + (", one HIP graph replay per step" if args.graph else ""),
+                          + (f", HIP graph replays of {args.graph_steps} step(s)" if args.graph else ""),
                  "algorithmic_bytes": ab, "gbs": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
                  "ms_per_step_median": float(np.median(step_ms)),
                  "ms_per_step_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
