@@ -314,7 +314,14 @@ def kernel_bytes(bench):
     # the large fused dispatch reads x into the Infinity Cache in its layout
     # launch (layout_prefetch) and again from there in its row kernel; the
     # algorithmic read of x belongs to the dispatch
+    # the two-launch layout of large batches: the rank kernel reads the ids,
+    # the index kernel writes both maps (their table and slot traffic is the
+    # workspace, not algorithmic)
     algo = {"combine_kernel": ab["combine"], "layout_single": ab["layout"], "layout_prefetch": ab["layout"]}
+    tk4 = bench.get("config", {}).get("tokens", 0) * bench.get("config", {}).get("topk", 0) * 4
+    if tk4:
+        algo["layout_rank"] = tk4
+        algo["layout_index"] = ab["layout"] - tk4
     for q in QUANT_TEMPLATE.values():
         algo[f"dispatch_rows_{q}"] = ab["dispatch"]
         algo[f"dispatch_fused_{q}"] = ab["dispatch"] + ab["layout"]
@@ -473,8 +480,10 @@ def summarize(run_dir, calib_mib):
                 lines += [f"Algorithmic bytes per launch: {a:,} B -> {a / (avg * 1e3):,.0f} GB/s at the traced "
                           f"average ({a / (avg * 1e3) / HBM_PEAK_GBS:.1%} of the 8 TB/s HBM peak).", ""]
         sep = {k: v for k, v in per_call.get("separate_calls_ms_mean", {}).items() if v}
+        step = (f"step {bench['ms_per_step'] * 1e3:.1f} us ({bench['config'].get('caches', '')}), "
+                if "ms_per_step" in bench else "")
         lines += [f"Benchmark line of the same build (`{bench_cmd}`), HIP events on the launch stream: "
-                  f"step {bench['ms_per_step'] * 1e3:.1f} us ({bench['config'].get('caches', '')}), per call "
+                  f"{step}per call "
                   + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in per_call["per_call_ms_mean"].items())
                   + ("" if not sep else "; separate calls (back to back) "
                      + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in sep.items())) + ".", ""]
