@@ -763,15 +763,20 @@ def main():
             layout_dispatch(st)
             combine(st)
 
-    def timed_steps(n, cold):
-        """n steps between two device synchronisations, each bracketed by HIP
-        events on the launch stream (and split at the dispatch/combine
-        boundary when eager); with `cold`, each step follows an untimed flush.
-        Returns per-step, per-dispatch and per-combine event times (ms) and the
-        wall time of the whole region (flushes included)."""
+    def timed_steps(n, cold, split=False):
+        """n steps between two device synchronisations.  With `cold`, each
+        step follows an untimed flush and is bracketed by HIP events on the
+        launch stream; back to back, two events bracket all n steps.  With
+        `split` (eager steps only), every step also gets an event between its
+        dispatch and combine calls, for the per-call times: an event between
+        two kernels waits for the first one's end-of-kernel cache write-back
+        (3-6 us on the DeepSeek-V3 prefill batch), so the step times come from
+        runs without one.  Returns per-step, per-dispatch and per-combine
+        event times (ms) and the wall time of the whole region (flushes
+        included)."""
         per = args.graph_steps if graph is not None else 1  # steps per replay
         n = -(-n // per)
-        beg, mid, end = new_events(n), new_events(n), new_events(n)
+        beg, mid, end = new_events(n), new_events(n) if split else None, new_events(n)
         flushed = None
         torch.cuda.synchronize()
         w0 = time.perf_counter()
@@ -779,30 +784,28 @@ def main():
         for i in range(n):
             if cold:
                 flushed = flush()
+            if cold or split or i == 0:
+                beg[i].record(stream)
             if graph is not None:
-                # back to back, replays carry no events of their own
-                if cold or i == 0:
-                    beg[i].record(stream)
                 graph.replay()
-                if cold or i == n - 1:
-                    end[i].record(stream)
-                continue
-            beg[i].record(stream)
-            layout_dispatch(stream)
-            mid[i].record(stream)
-            combine(stream)
-            end[i].record(stream)
-        if not cold:
+            else:
+                layout_dispatch(stream)
+                if split:
+                    mid[i].record(stream)
+                combine(stream)
+            if cold or split or i == n - 1:
+                end[i].record(stream)
+        if not cold and not split:
             enqueue_ms.append((time.perf_counter() - h0) * 1e3 / n)
         torch.cuda.synchronize()
         wall_s = time.perf_counter() - w0
         if flushed is not None:
             assert int(flushed.item()) == scratch.numel()
-        if cold:
+        if cold or split:
             step = [beg[i].elapsed_time(end[i]) / per for i in range(n)]
         else:  # back to back: the mean step is the span of all steps over their number
             step = [beg[0].elapsed_time(end[n - 1]) / (n * per)] * n
-        if graph is not None:
+        if not split:
             return step, None, None, wall_s
         return (step, [beg[i].elapsed_time(mid[i]) for i in range(n)],
                 [mid[i].elapsed_time(end[i]) for i in range(n)], wall_s)
@@ -820,24 +823,23 @@ def main():
     # --flush-mib 0 the headline steps run back to back instead.
     cold_headline = args.flush_mib > 0
     log(f"[bench] timing {args.steps} steps ({'each after a cache flush' if cold_headline else 'back to back'})")
-    step_ms, dispatch_ms, combine_ms, wall = timed_steps(args.steps, cold_headline)
+    step_ms, _, _, wall = timed_steps(args.steps, cold_headline)
     ms_step = float(np.mean(step_ms))
-    # secondary: the same number of steps back to back, timed by the wall
-    # clock between two synchronisations (the inputs stay cached from step to
-    # step: x is read by one dispatch and again by the next)
+    # secondary: the same number of steps back to back (the inputs stay
+    # cached from step to step as far as the traffic in between allows)
     warm = None
     if cold_headline and not args.no_warm:
         log(f"[bench] timing {args.steps} steps back to back (warm caches)")
-        w_step, w_disp, w_comb, w_wall = timed_steps(args.steps, False)
+        w_step, _, _, w_wall = timed_steps(args.steps, False)
         w_ms = float(np.mean(w_step))  # span of the back-to-back steps over their number (HIP events)
         warm = {"ms_per_step": w_ms, "wall_ms_per_step": w_wall * 1e3 / args.steps, "tokens_per_s": T / (w_ms * 1e-3)}
-        if w_disp is not None:
-            warm["per_call_ms_mean"] = {"layout+dispatch": float(np.mean(w_disp)),
-                                        "combine": float(np.mean(w_comb))}
-    if dispatch_ms is None:  # graph replays: per-call times from eager steps after the timed region
-        saved, graph = graph, None
-        _, dispatch_ms, combine_ms, _ = timed_steps(min(args.steps, 50), cold_headline)
-        graph = saved
+    # per-call times (and the roofline's combine duration): the same steps,
+    # eager, under the headline's cache condition, with an event between the
+    # calls of each step
+    log(f"[bench] timing {args.steps} steps with an event between the calls (per-call times)")
+    saved, graph = graph, None
+    split_step_ms, dispatch_ms, combine_ms, _ = timed_steps(args.steps, cold_headline, split=True)
+    graph = saved
 
     # after the timed region: the same step as separate calls, each bracketed
     # by events (back to back), for the per-call breakdown
@@ -916,6 +918,7 @@ def main():
                  "ms_per_step_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
                  "timed_region_wall_s": wall,
                  "per_call_ms_mean": per_ms, "per_call_ms_median": per_med,
+                 "ms_per_step_with_call_events": float(np.mean(split_step_ms)),
                  "per_call_ms_p10_p90": per_p10_p90, "per_call_gbs": gbs,
                  "separate_calls_ms_mean": sep, "separate_calls_gbs": sep_gbs,
                  "host_enqueue_ms_per_step": enqueue_ms[0] if enqueue_ms else None, "kept_pairs": n_kept,
