@@ -11,6 +11,10 @@
 // bytes the kernel moves.  Sizes follow the DeepSeek-V3 prefill batch: 117 MB
 // of token rows read, 4 x that written (dispatch, E4M3 rows of 8 pairs per
 // token: 470 MB); 8 x that read and 117 MB written (combine).
+//
+// The last section repeats the two mixes with buffer loads and stores whose
+// cache-policy bits (sc0 = 1, nt = 2, sc1 = 16 in the instruction's policy
+// operand) are set explicitly, one combination per case.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -115,6 +119,55 @@ __global__ __launch_bounds__(kThreads) void fan_in(const u32x4 *src, long n16, u
     }
 }
 
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle or index.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t resource(const void *p, long bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, kRawBufferWord3);
+}
+
+// dispatch's mix with explicit policies: x read with LOAD, 4 regions written with STORE
+template <int LOAD, int STORE>
+__global__ __launch_bounds__(kThreads) void fan_out_policy(const u32x4 *src, long n16, u32x4 *dst)
+{
+    const __amdgpu_buffer_rsrc_t rs = resource(src, n16 * 16);
+    __amdgpu_buffer_rsrc_t rd[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        rd[f] = resource(dst + (long)f * n16, n16 * 16);
+    const long stride = (long)gridDim.x * kThreads;
+    for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i * 16), 0, LOAD);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+            __builtin_amdgcn_raw_buffer_store_b128(a, rd[f], (int)(i * 16), 0, STORE);
+    }
+}
+
+// combine's mix with explicit policies: 8 regions read with LOAD, their xor written with STORE
+template <int LOAD, int STORE>
+__global__ __launch_bounds__(kThreads) void fan_in_policy(const u32x4 *src, long n16, u32x4 *dst)
+{
+    __amdgpu_buffer_rsrc_t rs[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+        rs[f] = resource(src + (long)f * n16, n16 * 16);
+    const __amdgpu_buffer_rsrc_t rd = resource(dst, n16 * 16);
+    const long stride = (long)gridDim.x * kThreads;
+    for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            v[f] = __builtin_amdgcn_raw_buffer_load_b128(rs[f], (int)(i * 16), 0, LOAD);
+        u32x4 acc = v[0];
+#pragma unroll
+        for (int f = 1; f < 8; ++f)
+            acc ^= v[f];
+        __builtin_amdgcn_raw_buffer_store_b128(acc, rd, (int)(i * 16), 0, STORE);
+    }
+}
+
 int main()
 {
     const long xb = 117440512L;  // token rows of the DeepSeek-V3 prefill batch: 8192 x 7168 bf16
@@ -176,5 +229,29 @@ int main()
         run("combine mix: read 8 x (940 MB), write 117 MB", 9 * xb,
             [&] { hipLaunchKernelGGL(fan_in<8>, dim3(grid), dim3(kThreads), 0, 0, big, n16, x); });
     }
+    // cache policies (buffer instructions, grid 2048); every region is 117 MB < 2^31 bytes
+    printf("cache policies: load bits / store bits (sc0 = 1, nt = 2, sc1 = 16), grid 2048\n");
+    const int grid = 2048;
+#define FAN_OUT(L, S)                                                                                   \
+    run("dispatch mix, load " #L ", store " #S, 5 * xb,                                               \
+        [&] { hipLaunchKernelGGL((fan_out_policy<L, S>), dim3(grid), dim3(kThreads), 0, 0, x, n16, big); })
+#define FAN_IN(L, S)                                                                                    \
+    run("combine mix, load " #L ", store " #S, 9 * xb,                                                \
+        [&] { hipLaunchKernelGGL((fan_in_policy<L, S>), dim3(grid), dim3(kThreads), 0, 0, big, n16, x); })
+    FAN_OUT(0, 2);
+    FAN_OUT(0, 18);
+    FAN_OUT(0, 19);
+    FAN_OUT(0, 0);
+    FAN_OUT(0, 16);
+    FAN_OUT(2, 2);
+    FAN_OUT(16, 2);
+    FAN_IN(2, 0);
+    FAN_IN(2, 2);
+    FAN_IN(2, 16);
+    FAN_IN(2, 17);
+    FAN_IN(2, 18);
+    FAN_IN(0, 16);
+    FAN_IN(16, 16);
+    FAN_IN(18, 16);
     return 0;
 }
