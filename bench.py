@@ -242,17 +242,44 @@ def run_dedup(args, wl, cfg, d_idx, d_w, d_x, d_y, d_out, bufs, stream):
     }
 
 
+def code_text(source):
+    """C/C++ source with its comments removed and every run of whitespace
+    reduced to one space: comment and layout edits leave it unchanged, any
+    change to the code does not."""
+    out, i, n = [], 0, len(source)
+    while i < n:
+        c = source[i]
+        if source.startswith("//", i):
+            j = source.find("\n", i)
+            i = n if j < 0 else j
+        elif source.startswith("/*", i):
+            j = source.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":  # string or character literal, escapes included
+            j = i + 1
+            while j < n and source[j] != c:
+                j += 2 if source[j] == "\\" else 1
+            out.append(source[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def library_hash():
-    """sha256 over every source the library is built from (kernels, launch
-    plans, ABI): counter figures taken on another build are not reused."""
+    """sha256 over the code (comments and whitespace removed, see code_text)
+    of every source the library is built from (kernels, launch plans, ABI):
+    counter figures taken on other code are not reused."""
     h = hashlib.sha256()
     for sub in (("include",), ("combine_topk_idx_amd", "csrc")):
         d = os.path.join(ROOT, *sub)
         for name in sorted(os.listdir(d)):
             if name.endswith((".h", ".hip")):
                 h.update(name.encode())
-                with open(os.path.join(d, name), "rb") as f:
-                    h.update(f.read())
+                with open(os.path.join(d, name), encoding="utf-8") as f:
+                    h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

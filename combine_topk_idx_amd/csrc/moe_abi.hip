@@ -604,8 +604,9 @@ moe_status_t moe_combine_partial(const moe_config_t *cfg, int32_t num_tokens, co
     a.E = cfg->num_experts;
     a.R = cfg->num_ranks;
     a.L = cfg->num_experts / cfg->num_ranks;
-    // plain stores: the reduction reads the partial rows right away (streaming
-    // them measured 242 -> 254 us here at the DeepSeek-V3 prefill shape)
+    // device-scope stores that leave the partial rows in the Infinity Cache:
+    // the reduction reads them right away (streaming them measured
+    // 242 -> 254 us here at the DeepSeek-V3 prefill shape)
     a.stream_out = 0;
     return from_hip(launch_combine_partial(a, static_cast<hipStream_t>(stream)));
 }

@@ -31,8 +31,9 @@ constexpr int kVecs = kCombineWidth / (kWave * 8);  // 16-byte vectors per lane 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Expert outputs are read exactly once: non-temporal loads keep them from
-// displacing useful lines in L2 and the MALL (measured ~13% faster than
-// plain loads on the DeepSeek-V3 prefill shape).
+// displacing useful lines in L2 and the MALL (a streaming kernel with the
+// DeepSeek-V3 prefill combine's traffic: 176.5 us, against 204 us with plain
+// loads and 204-209 us with any coherence-scope bit on the loads).
 __device__ __forceinline__ uint4 load_stream(const uint16_t *p)
 {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -55,8 +56,9 @@ constexpr int kStoreDeviceScope = 16;
 // Otherwise the stores carry the device coherence scope: on gfx950 they are
 // written through L2 to the memory-side cache instead of staying dirty in L2
 // until the write-back at the end of the kernel, which the next kernel waits
-// for (DeepSeek-V3 prefill combine, 117 MB out: 182.7 -> 177.3 us, and a
-// plain streaming kernel with this mix 178.7 -> 174.4 us).
+// for (DeepSeek-V3 prefill combine, 117 MB out: 182.7 -> 177.3 us; a
+// streaming kernel with this mix: 181 us plain, 176.5 us device scope, 188 us
+// non-temporal).
 template <bool NT>
 __device__ __forceinline__ void store_row(uint16_t *row, int32_t H, const int (&col)[kVecs],
                                           const bool (&active)[kVecs], float (&acc)[kVecs][8])

@@ -80,6 +80,17 @@ def test_library_hash_is_stable():
     assert len(bench.library_hash()) == 64
 
 
+def test_code_text_ignores_comments_not_code():
+    src = 'int a = 1; // note\n/* block\n comment */ int b = 2;\nconst char *s = "// kept";\nchar c = \'\\\'\';\n'
+    edited_comment = src.replace("note", "another note").replace("block", "other")
+    relaid = src.replace("int b = 2;", "int   b =\n 2;")
+    changed_code = src.replace("int b = 2;", "int b = 3;")
+    assert bench.code_text(src) == bench.code_text(edited_comment) == bench.code_text(relaid)
+    assert bench.code_text(src) != bench.code_text(changed_code)
+    assert '"// kept"' in bench.code_text(src)
+    assert "note" not in bench.code_text(src) and "comment" not in bench.code_text(src)
+
+
 def test_bench_refuses_more_than_one_gpu(tmp_path):
     import subprocess
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
