@@ -305,9 +305,10 @@ QUANT_TEMPLATE = {"0": "bf16", "1": "fp8_f32", "2": "fp8_ue8m0", "3": "mxfp8"}
 
 def short_kernel(name):
     """'void moe::(anonymous namespace)::dispatch_rows<2>(moe::DispatchArgs)'
-    -> 'dispatch_rows_fp8_ue8m0'; combine_kernel<false, NT> -> 'combine_kernel',
-    combine_kernel<true, NT> -> 'combine_kernel_partial' (NT = streamed output
-    stores, not a separate kernel); rank_layout_kernel<KV> (KV = id vectors per
+    -> 'dispatch_rows_fp8_ue8m0'; combine_kernel<false, ...> -> 'combine_kernel',
+    combine_kernel<true, ...> -> 'combine_kernel_partial' (the other arguments
+    pick streamed output stores and loads, not a separate kernel);
+    rank_layout_kernel<KV> (KV = id vectors per
     token, not a format) -> 'rank_layout_kernel'."""
     base = name.split("(moe::")[0].split("::")[-1]
     named = {"repack_kernel<true>": "repack_to_contiguous", "repack_kernel<false>": "repack_to_masked",

@@ -465,6 +465,7 @@ moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint
     a.token_rank_row = nullptr;
     a.E = a.R = a.L = 0;
     a.stream_out = (int64_t)num_tokens * cfg->hidden * 2 > kCombineStreamOutBytes;
+    a.stream_in = (int64_t)num_tokens * cfg->num_topk * cfg->hidden * 2 > kCombineStreamInBytes;
     return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -608,6 +609,7 @@ moe_status_t moe_combine_partial(const moe_config_t *cfg, int32_t num_tokens, co
     // the reduction reads them right away (streaming them measured
     // 242 -> 254 us here at the DeepSeek-V3 prefill shape)
     a.stream_out = 0;
+    a.stream_in = (int64_t)num_tokens * cfg->num_topk * cfg->hidden * 2 > kCombineStreamInBytes;
     return from_hip(launch_combine_partial(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -636,6 +638,7 @@ moe_status_t moe_combine_reduce(const moe_config_t *cfg, int32_t num_tokens, con
     a.token_rank_row = nullptr;
     a.E = a.R = a.L = 0;
     a.stream_out = (int64_t)num_tokens * cfg->hidden * 2 > kCombineStreamOutBytes;
+    a.stream_in = (int64_t)num_tokens * cfg->num_ranks * cfg->hidden * 2 > kCombineStreamInBytes;
     return from_hip(launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -6,8 +6,9 @@
 //
 // Token-major: a wave owns a token (or a run of its columns).  The token's
 // kept rows and weights are compacted once into lanes 0..n-1 (ds_permute),
-// then every 1024-column iteration issues two non-temporal 16-byte loads per
-// kept row (up to 16 in flight per lane), accumulates in ascending k in fp32 with the product
+// then every 1024-column iteration issues two 16-byte loads per kept row (up
+// to 16 in flight per lane; non-temporal when the combine reads more than
+// 64 MiB), accumulates in ascending k in fp32 with the product
 // and the sum each rounded (no FMA), and stores 8 bf16 (round to nearest even,
 // v_cvt_pk_bf16_f32) as 16-byte vectors, written through L2 (device-scope
 // buffer stores) or, for outputs larger than half the Infinity Cache,
@@ -30,13 +31,21 @@ constexpr int kVecs = kCombineWidth / (kWave * 8);  // 16-byte vectors per lane 
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Expert outputs are read exactly once: non-temporal loads keep them from
-// displacing useful lines in L2 and the MALL (a streaming kernel with the
-// DeepSeek-V3 prefill combine's traffic: 176.5 us, against 204 us with plain
-// loads and 204-209 us with any coherence-scope bit on the loads).
-__device__ __forceinline__ uint4 load_stream(const uint16_t *p)
+// Expert outputs are read exactly once.  Large reads (NT) use non-temporal
+// loads, which keep them from displacing useful lines in L2 and the MALL (a
+// streaming kernel with the DeepSeek-V3 prefill combine's traffic: 176.5 us,
+// against 204 us with plain loads and 204-209 us with any coherence-scope bit
+// on the loads).  Small reads use plain loads, which find rows that are still
+// in the Infinity Cache and leave them there (DeepSeek-V3 decode: combine 6.9
+// -> 6.4 us, a 20-step graph step 14.4-15.1 -> 14.0 us).
+template <bool NT>
+__device__ __forceinline__ uint4 load_row(const uint16_t *p)
 {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    u32x4 v;
+    if constexpr (NT)
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    else
+        v = *reinterpret_cast<const u32x4 *>(p);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -101,7 +110,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const uint4
     }
 }
 
-template <bool PARTIAL, bool NT>
+template <bool PARTIAL, bool NT, bool NT_IN>
 __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 #pragma unroll
                         for (int s = 0; s < kVecs; ++s)
                             if (active[s])
-                                v[j][s] = load_stream(src + col[s]);
+                                v[j][s] = load_row<NT_IN>(src + col[s]);
                     }
                 }
 #pragma unroll
@@ -209,22 +218,33 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(CombineArgs a)
 
 }  // namespace
 
+namespace {
+
+template <bool PARTIAL>
+hipError_t launch_combine_kernel(const CombineArgs &a, hipStream_t stream)
+{
+    const dim3 grid(a.plan.grid), block(kBlockThreads);
+    if (a.stream_out && a.stream_in)
+        hipLaunchKernelGGL((combine_kernel<PARTIAL, true, true>), grid, block, 0, stream, a);
+    else if (a.stream_out)
+        hipLaunchKernelGGL((combine_kernel<PARTIAL, true, false>), grid, block, 0, stream, a);
+    else if (a.stream_in)
+        hipLaunchKernelGGL((combine_kernel<PARTIAL, false, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<PARTIAL, false, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
 {
-    if (a.stream_out)
-        hipLaunchKernelGGL((combine_kernel<false, true>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((combine_kernel<false, false>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_combine_kernel<false>(a, stream);
 }
 
 hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream)
 {
-    if (a.stream_out)
-        hipLaunchKernelGGL((combine_kernel<true, true>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((combine_kernel<true, false>), dim3(a.plan.grid), dim3(kBlockThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_combine_kernel<true>(a, stream);
 }
 
 }  // namespace moe

@@ -108,6 +108,7 @@ struct CombineArgs {
     const int32_t *token_rank_row;
     int32_t E, R, L;
     int32_t stream_out;          // non-temporal output stores (outputs larger than kCombineStreamOutBytes)
+    int32_t stream_in;           // non-temporal loads of y (reads larger than kCombineStreamInBytes)
 };
 
 // ---- per-rank (deduplicated) exchange --------------------------------------
@@ -214,5 +215,11 @@ constexpr int kCombineMinItemsPerToken = 8;      // about 1024 columns per item:
 // Token rows up to this size are prefetched into it by a large fused dispatch.
 constexpr int64_t kHalfInfinityCacheBytes = (int64_t)128 << 20;
 constexpr int64_t kCombineStreamOutBytes = kHalfInfinityCacheBytes;
+// Combines that read at most this many bytes of expert outputs (T * K rows)
+// load them with plain, cache-allocating loads: decode-sized outputs are
+// served from the Infinity Cache when the kernel that wrote them (or the
+// previous step) left them there.  Larger reads stream through with
+// non-temporal loads, which do not allocate and are faster for them.
+constexpr int64_t kCombineStreamInBytes = (int64_t)64 << 20;
 
 }  // namespace moe
