@@ -10,7 +10,8 @@
 // Prints one line per case: median of 15 event-timed launches, GB/s of the
 // bytes the kernel moves.  Sizes follow the DeepSeek-V3 prefill batch: 117 MB
 // of token rows read, 4 x that written (dispatch, E4M3 rows of 8 pairs per
-// token: 470 MB); 8 x that read and 117 MB written (combine).
+// token: 470 MB); 8 x that read and 117 MB written (combine); 2 x that read
+// and 4 x written (the per-rank expansion: about 4 ranks per token).
 //
 // The last section repeats the two mixes with buffer loads and stores whose
 // cache-policy bits (sc0 = 1, nt = 2, sc1 = 16 in the instruction's policy
@@ -97,6 +98,24 @@ __global__ __launch_bounds__(kThreads) void fan_out(const u32x4 *src, long n16, 
 #pragma unroll
         for (int f = 0; f < F; ++f)
             __builtin_nontemporal_store(a, dst + (long)f * n16 + i);
+    }
+}
+
+// the per-rank expansion's mix: S source regions (src + s * n16, read with
+// non-temporal loads), each stored to D / S destination regions (dst + d *
+// n16) with non-temporal stores
+template <int S, int D>
+__global__ __launch_bounds__(kThreads) void fan_out_sources(const u32x4 *src, long n16, u32x4 *dst)
+{
+    const long stride = (long)gridDim.x * kThreads;
+    for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+        u32x4 v[S];
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+            v[k] = __builtin_nontemporal_load(src + (long)k * n16 + i);
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            __builtin_nontemporal_store(v[d % S], dst + (long)d * n16 + i);
     }
 }
 
@@ -228,6 +247,10 @@ int main()
             [&] { hipLaunchKernelGGL(fan_out<4>, dim3(grid), dim3(kThreads), 0, 0, x, n16, big); });
         run("combine mix: read 8 x (940 MB), write 117 MB", 9 * xb,
             [&] { hipLaunchKernelGGL(fan_in<8>, dim3(grid), dim3(kThreads), 0, 0, big, n16, x); });
+        // sources in regions 4-5 of big, destinations in regions 0-3
+        run("expansion mix: read 235 MB, write 2 x (470 MB)", 6 * xb, [&] {
+            hipLaunchKernelGGL((fan_out_sources<2, 4>), dim3(grid), dim3(kThreads), 0, 0, big + 4 * n16, n16, big);
+        });
     }
     // cache policies (buffer instructions, grid 2048); every region is 117 MB < 2^31 bytes
     printf("cache policies: load bits / store bits (sc0 = 1, nt = 2, sc1 = 16), grid 2048\n");
