@@ -95,6 +95,7 @@ constexpr int kFusedMaxExperts = 512;   // keeps the fused block's LDS within 44
 constexpr int kPrefetchMinTokensPerCu = 8;  // from this many tokens per compute unit, a fused call prefetches x
 constexpr int kPrefetchSegment = 64;        // bytes of x each prefetch load stands for (one per segment)
 constexpr int kPrefetchBatch = 16;          // prefetch loads per lane in flight before the wave waits
+constexpr int kPrefetchSkipTenths = 3;      // tenths of the tokens, from the first, a fused call does not prefetch
 
 struct CombineArgs {
     const uint16_t *y;
