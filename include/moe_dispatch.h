@@ -216,10 +216,11 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
  * its pairs while they are in flight.  Large batches (at least 8 tokens per
  * compute unit) whose token rows x fit in half of the 256 MB Infinity Cache
  * instead run two kernels, unless num_cus > 0: the one-launch layout, with
- * the compute units it leaves idle reading x into the Infinity Cache
- * meanwhile, then the row kernel of moe_dispatch over every compute unit.  So
- * a call whose x was evicted from the caches reads it from HBM while the
- * layout runs, not behind its own row stores.  Batches beyond the one-launch
+ * the compute units it leaves idle reading x (the rows of all but the first
+ * 3/10 of the tokens) into the Infinity Cache meanwhile, then the row kernel
+ * of moe_dispatch over every compute unit.  So a call whose x was evicted
+ * from the caches reads most of it from HBM while the layout runs, not behind
+ * its own row stores.  Batches beyond the one-launch
  * limits run the layout and dispatch kernels back to back.
  */
 moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
@@ -240,9 +241,13 @@ moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, con
  * out[t,:] = bf16_RNE( sum over k ascending with row = pair_to_row[t*K+k] >= 0
  * of topk_w[t*K+k] * y[row,:] ), accumulated in fp32 from +0 with the product
  * and the sum each rounded to fp32.  A token with no kept pair gives +0.
- * An out larger than 128 MiB is written with non-temporal stores (it cannot
- * stay in the 256 MB Infinity Cache); a smaller one stays cacheable for the
- * kernel that reads it next.
+ * Cache use: reads of at most 64 MiB of y (num_tokens * K rows) use
+ * cache-allocating loads, so decode-sized outputs still in the Infinity Cache
+ * are found there; larger reads stream with non-temporal loads.  An out larger
+ * than 128 MiB is written with non-temporal stores (it cannot stay in the
+ * 256 MB Infinity Cache); a smaller one with device-scope stores, which go
+ * through L2 to the Infinity Cache and stay there for the kernel that reads it
+ * next.
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_CAPACITY, MOE_ERR_HIP.
  */
 moe_status_t moe_combine(const moe_config_t *cfg, int32_t num_tokens, const uint16_t *y,
