@@ -247,7 +247,6 @@ class DispatchBuffers:
             self.out_scale = None
         else:
             self.out_x = torch.empty((self.rows, H), dtype=torch.uint8, device=device)
-            nb = H // 128
             self.out_scale = _scale_buffer(cfg, self.rows, device)
         self.out_row_weight = (torch.empty(self.rows, dtype=torch.float32, device=device)
                                if row_weight else None)
@@ -281,7 +280,6 @@ def moe_dispatch_layout_noalloc(cfg: MoeConfig, num_tokens: int, topk_idx: torch
 def _dispatch_ptrs(cfg, num_tokens, x, topk_w, out_x, out_scale, out_row_weight):
     rows = moe_rows_capacity(cfg)
     H, K = cfg.hidden, cfg.num_topk
-    nb = H // 128
     xp = _ptr(x, 2, num_tokens * H, "x") if num_tokens > 0 else None
     wp = _ptr(topk_w, 4, num_tokens * K if out_row_weight is not None else 0, "topk_w")
     ob = 2 if cfg.quant == QUANT_NONE else 1
