@@ -37,8 +37,8 @@ struct LayoutArgs {
     int32_t *slots;     // [P] slot of each pair among its expert's pairs inside its block
     moe_handle_t h;
     // one-launch layout only: pf_blocks blocks after nblocks prefetch the
-    // token rows x [pf_T, pf_H] of the dispatch that follows into the
-    // Infinity Cache
+    // token rows pf_x [pf_T, pf_H] (the later tokens of the dispatch that
+    // follows) into the Infinity Cache
     const uint16_t *pf_x = nullptr;
     int32_t pf_T = 0, pf_H = 0, pf_blocks = 0;
 };
