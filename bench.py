@@ -564,7 +564,8 @@ def summarize(run_dir, calib_mib):
     print(f"wrote {TRAFFIC_FILE} and summaries for {sorted(per_kernel)}")
 
 
-CPU_BASELINE_REPEATS = 3
+CPU_BASELINE_REPEATS = 3         # oracle passes per leg, prefill-sized samples
+CPU_BASELINE_REPEATS_SMALL = 10  # decode-sized samples (at most 1024 tokens)
 
 
 def cpu_model():
@@ -596,12 +597,14 @@ def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
     `max_tokens` tokens of the same batch, layout + dispatch + combine, timed
     on one thread and with the token loops of dispatch and combine split over
     all host cores (OpenMP; the layout stays serial), median of
-    CPU_BASELINE_REPEATS passes each.
+    CPU_BASELINE_REPEATS passes each (CPU_BASELINE_REPEATS_SMALL for samples of
+    at most 1024 tokens).
     When the sample is the whole batch and `gpu` holds the benchmark's final
     outputs (host copies), they are checked against the oracle's: layout and
     dispatched bytes bit for bit, combine within |g - o| <= 1e-2 |o| + 1e-5 S."""
     import oracle
     T = min(wl.T, max_tokens)
+    repeats = CPU_BASELINE_REPEATS_SMALL if T <= 1024 else CPU_BASELINE_REPEATS
     sub = wl.replace(T=T)
     idx, w, x = inp.topk_idx[:T], inp.topk_w[:T], inp.x[:T]
     rows = sub.rows_capacity
@@ -616,7 +619,7 @@ def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
         used = oracle.set_threads(threads)
         times = []
         try:
-            for _ in range(CPU_BASELINE_REPEATS):
+            for _ in range(repeats):
                 t0 = time.perf_counter()
                 out = one_pass()
                 times.append(time.perf_counter() - t0)
@@ -629,7 +632,7 @@ def cpu_baseline(wl, inp, y, max_tokens, gpu=None):
     one_used, one_s, (h, ox, osc, out) = leg(1)
     res = {"value": T / all_s, "unit": "tokens/s", "cores": all_used, "kind": "oracle",
            "sample": f"first {T} of {wl.T} tokens of the same batch, layout + dispatch + combine, median of "
-                     f"{CPU_BASELINE_REPEATS} passes ({all_s:.2f} s each) with dispatch and combine split over "
+                     f"{repeats} passes ({all_s:.2f} s each) with dispatch and combine split over "
                      f"{all_used} OpenMP threads (layout serial)",
            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
            "gbs": None, "single_thread": {"value": T / one_s, "unit": "tokens/s", "cores": one_used,
