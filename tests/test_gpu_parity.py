@@ -410,6 +410,19 @@ def test_fewer_tokens_than_max_and_num_cus(fused):
     check_parity(wl, idx, w, x, y, cfg, "T<max, num_cus=7", fused)
 
 
+@pytest.mark.parametrize("T", [2048, 2049])
+def test_combine_load_policy_boundary(T):
+    """Combines reading at most 64 MiB of expert rows (T*K*H*2) use cache-
+    allocating loads, larger ones non-temporal loads: both sides of the switch
+    (exactly 64 MiB and one token more) against the oracle."""
+    wl = W.WORKLOADS["qwen3moe_decode_T128"].replace(T=T, layout=W.LAYOUT_CONTIGUOUS, align=16,
+                                                     quant=W.QUANT_NONE)
+    assert wl.K * wl.H * 2 * 2048 == 64 << 20
+    _say(f"combine load-policy boundary T={T} H={wl.H} K={wl.K}")
+    idx, w, x, y = inputs_for(wl)
+    check_parity(wl, idx, w, x, y, make_cfg(wl), f"load-policy boundary T={T}")
+
+
 def test_fused_unaligned_ids():
     """topk_idx that is only 4-byte aligned takes the scalar histogram path."""
     wl = W.Workload("unaligned", T=300, H=512, E=32, K=4, R=4, layout=W.LAYOUT_CONTIGUOUS,
