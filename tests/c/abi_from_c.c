@@ -68,6 +68,66 @@ int main(void)
     CHECK(moe_combine(&c, 16, (const uint16_t *)fake, (const float *)fake, &hb, (uint16_t *)fake, NULL) ==
           MOE_ERR_INVALID_ARG);
 
+    /* status names: every code, and any other int */
+    CHECK(strcmp(moe_status_str(MOE_OK), "MOE_OK") == 0);
+    CHECK(strcmp(moe_status_str(MOE_ERR_HIP), "MOE_ERR_HIP") == 0);
+    CHECK(strcmp(moe_status_str((moe_status_t)-1), "MOE_ERR_UNKNOWN") == 0);
+    CHECK(strcmp(moe_status_str((moe_status_t)100000), "MOE_ERR_UNKNOWN") == 0);
+
+    /* the remaining entry points: host-side errors and empty calls */
+    moe_config_t m = c;
+    m.layout = MOE_LAYOUT_MASKED;
+    m.capacity = 256;
+    m.align = 1;
+    moe_config_t bf = c;
+    bf.quant = MOE_QUANT_NONE;
+    moe_rank_handle_t rh = {fake, fake, fake, fake};
+    CHECK(moe_dispatch_layout_noalloc(&c, 8193, fake, &h, NULL) == MOE_ERR_CAPACITY);
+    CHECK(moe_dispatch_layout_noalloc(&c, 16, NULL, &h, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_dispatch_layout_noalloc(&c, 16, (const int32_t *)((const char *)fake + 1), &h, NULL) ==
+          MOE_ERR_INVALID_ARG); /* misaligned ids */
+    CHECK(moe_dispatch_layout_noalloc(&c, 16, fake, NULL, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_dispatch_layout_noalloc(NULL, 16, fake, &h, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_dispatch_fused(&c, 8193, fake, (const uint16_t *)fake, NULL, &h, fake, 1u << 20, fake, fake, NULL,
+                             NULL) == MOE_ERR_CAPACITY);
+    CHECK(moe_dispatch_fused(&c, 16, NULL, (const uint16_t *)fake, NULL, &h, fake, 1u << 20, fake, fake, NULL,
+                             NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_rank_layout(&c, 16, fake, NULL, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_rank_layout(&c, 16, NULL, &rh, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_rank_layout(&c, 8193, fake, &rh, NULL) == MOE_ERR_CAPACITY);
+    CHECK(moe_dispatch_dedup(&c, 16, NULL, &rh, fake, fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_dispatch_dedup(&c, 16, (const uint16_t *)fake, &rh, fake, NULL, NULL) ==
+          MOE_ERR_INVALID_ARG); /* FP8 needs send_scale */
+    CHECK(moe_expand(&c, 16, fake, fake, fake, &rh, &h, NULL, fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_combine_partial(&c, 16, fake, (const uint16_t *)fake, (const float *)fake, &h, &rh, NULL, NULL) ==
+          MOE_ERR_INVALID_ARG);
+    CHECK(moe_combine_reduce(&c, 16, NULL, &rh, (uint16_t *)fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_combine_reduce(&c, 0, NULL, &rh, NULL, NULL) == MOE_OK);
+    CHECK(moe_row_expert(&c, &h, NULL, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_row_expert(&c, NULL, fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_repack_rows_capacity(&m, 128) == (size_t)256 * 256 + 256 * 127);
+    CHECK(moe_repack_rows_capacity(&m, 0) == 0);
+    CHECK(moe_repack_rows_capacity(&c, 128) == 0); /* needs a masked config */
+    CHECK(moe_repack_masked_to_contiguous(&c, 128, &h, fake, fake, fake, fake, fake, fake, NULL) ==
+          MOE_ERR_INVALID_ARG);
+    CHECK(moe_repack_masked_to_contiguous(&m, 128, &h, NULL, fake, fake, fake, fake, fake, NULL) ==
+          MOE_ERR_INVALID_ARG);
+    CHECK(moe_repack_masked_to_contiguous(&m, 0, &h, fake, fake, fake, fake, fake, fake, NULL) ==
+          MOE_ERR_INVALID_ARG);
+    CHECK(moe_repack_contiguous_to_masked(&c, &h, fake, (const uint16_t *)fake, (uint16_t *)fake, NULL) ==
+          MOE_ERR_INVALID_ARG);
+    CHECK(moe_repack_contiguous_to_masked(&m, &h, NULL, (const uint16_t *)fake, (uint16_t *)fake, NULL) ==
+          MOE_ERR_INVALID_ARG);
+    CHECK(moe_scale_words(&bf) == 0);
+    CHECK(moe_scales_mn_major(&c, -1, fake, fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_scales_mn_major(&bf, 16, fake, fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_scales_mn_major(&c, 16, NULL, fake, NULL) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_scales_mn_major(&c, 0, fake, fake, NULL) == MOE_OK);
+    moe_config_t many = c;
+    many.num_ranks = 64; /* the per-rank exchange takes at most 32 ranks */
+    CHECK(moe_rank_rows_capacity(&many) == 0);
+    CHECK(moe_rank_layout(&many, 16, fake, &rh, NULL) == MOE_ERR_UNSUPPORTED);
+
     if (failures == 0)
         printf("C ABI checks passed\n");
     return failures == 0 ? 0 : 1;
