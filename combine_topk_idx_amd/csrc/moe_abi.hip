@@ -428,7 +428,10 @@ moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, con
         f.tokens_per_block = fp.tokens_per_block;
         return from_hip(launch_dispatch_fused(f, cfg->quant, s));
     }
-    // batches the one-launch kernel does not take: the two calls back to back
+    // batches the one-launch kernel does not take: the two calls back to back,
+    // large ones with part of x prefetched by the layout kernels
+    if (num_tokens > 0)
+        split_prefetch_plan(da, lp, cfg->num_cus, la);
     hipError_t e = launch_layout(la, lp, s);
     if (e == hipSuccess && num_tokens > 0)
         e = launch_dispatch(da, cfg->quant, s);

@@ -36,11 +36,14 @@ struct LayoutArgs {
     int32_t *ws;        // [E + 1][kLayoutMaxBlocks] per-block histograms (row E: invalid ids)
     int32_t *slots;     // [P] slot of each pair among its expert's pairs inside its block
     moe_handle_t h;
-    // one-launch layout only: pf_blocks blocks after nblocks prefetch the
-    // token rows pf_x [pf_T, pf_H] (the later tokens of the dispatch that
-    // follows) into the Infinity Cache
+    // fused large-batch dispatch: pf_blocks blocks after nblocks prefetch
+    // token rows of the dispatch that follows into the Infinity Cache -- in
+    // the one-launch layout pf_x [pf_T, pf_H]; in the two-launch layout the
+    // rank kernel pf_x [pf_T, pf_H] and the index kernel pf2_x [pf2_T, pf_H]
     const uint16_t *pf_x = nullptr;
     int32_t pf_T = 0, pf_H = 0, pf_blocks = 0;
+    const uint16_t *pf2_x = nullptr;
+    int32_t pf2_T = 0;
 };
 
 struct LayoutPlan {
@@ -96,6 +99,11 @@ constexpr int kPrefetchMinTokensPerCu = 8;  // from this many tokens per compute
 constexpr int kPrefetchSegment = 64;        // bytes of x each prefetch load stands for (one per segment)
 constexpr int kPrefetchBatch = 16;          // prefetch loads per lane in flight before the wave waits
 constexpr int kPrefetchSkipTenths = 3;      // tenths of the tokens, from the first, a fused call does not prefetch
+// Token-row bytes the rank and the index kernel of the two-launch layout
+// prefetch in a fused call whose rows do not fit the one-launch plan: about
+// what HBM streams while each kernel runs (4 and 8 us), 100 MB in all.
+constexpr int64_t kRankPrefetchBytes = (int64_t)40 << 20;
+constexpr int64_t kIndexPrefetchBytes = (int64_t)60 << 20;
 
 struct CombineArgs {
     const uint16_t *y;
@@ -193,6 +201,7 @@ RowPlan row_plan(int32_t T, int32_t H, int32_t width, int32_t max_iters_per_item
 hipError_t launch_dispatch(const DispatchArgs &a, int32_t quant, hipStream_t stream);
 bool fused_plan(int32_t T, int32_t K, int32_t H, int32_t E, int32_t quant, int32_t num_cus, FusedPlan &fp);
 bool fused_prefetch_plan(const DispatchArgs &d, const LayoutPlan &lp, int32_t num_cus, LayoutArgs &la);
+bool split_prefetch_plan(const DispatchArgs &d, const LayoutPlan &lp, int32_t num_cus, LayoutArgs &la);
 hipError_t launch_dispatch_fused(const FusedArgs &f, int32_t quant, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 hipError_t launch_combine_partial(const CombineArgs &a, hipStream_t stream);

@@ -83,6 +83,10 @@ __device__ __forceinline__ void load_runs(int32_t (&v)[kTileRounds], const int32
 
 __global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
 {
+    if ((int)blockIdx.x >= a.nblocks) {  // prefetch blocks of a fused call
+        dev::prefetch_rows(a.pf_x, a.pf_T, a.pf_H, blockIdx.x - a.nblocks, a.pf_blocks);
+        return;
+    }
     extern __shared__ int32_t cnt[];  // [WB][E]: per-wave counts, then per-wave slot bases
     __shared__ int32_t red[kMaxBlockWaves];
     const int E = a.E;
@@ -193,6 +197,10 @@ __global__ __launch_bounds__(1024) void layout_rank(LayoutArgs a)
 
 __global__ __launch_bounds__(1024) void layout_index(LayoutArgs a)
 {
+    if ((int)blockIdx.x >= a.nblocks) {  // prefetch blocks of a fused call
+        dev::prefetch_rows(a.pf2_x, a.pf2_T, a.pf_H, blockIdx.x - a.nblocks, a.pf_blocks);
+        return;
+    }
     extern __shared__ int32_t lds[];
     const int E = a.E;
     int32_t *tot = lds;          // [E+1] pairs per expert, all blocks ([E]: invalid ids)
@@ -336,12 +344,17 @@ hipError_t launch_layout(const LayoutArgs &a, const LayoutPlan &plan, hipStream_
             hipLaunchKernelGGL(layout_single<false>, grid, block, lds, stream, a);
         return hipGetLastError();
     }
+    // prefetch blocks (a fused call, split_prefetch_plan) run the same block
+    // size as prefetch_rows assumes
+    const bool pf = a.pf_blocks > 0 && plan.waves * kWave == kSingleThreads;
     if (a.P > 0) {
         const size_t lds = sizeof(int32_t) * (size_t)plan.waves * a.E;
-        hipLaunchKernelGGL(layout_rank, grid, block, lds, stream, a);
+        const int extra = pf && a.pf_T > 0 ? a.pf_blocks : 0;
+        hipLaunchKernelGGL(layout_rank, dim3(a.nblocks + extra), block, lds, stream, a);
     }
     const size_t lds = sizeof(int32_t) * (size_t)(3 * a.E + 4);
-    hipLaunchKernelGGL(layout_index, grid, block, lds, stream, a);
+    const int extra = pf && a.pf2_T > 0 ? a.pf_blocks : 0;
+    hipLaunchKernelGGL(layout_index, dim3(a.nblocks + extra), block, lds, stream, a);
     return hipGetLastError();
 }
 
