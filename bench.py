@@ -338,6 +338,23 @@ def short_kernel(name):
     return base
 
 
+# Kernels of a fused call that also carry prefetch blocks: their counted bytes
+# include token rows read ahead into the Infinity Cache, which the method reads
+# once and which count in the dispatch's algorithmic bytes.
+PREFETCH_NOTES = {
+    "layout_prefetch": "Most of these bytes are the prefetch blocks of the fused call reading the token rows x "
+                       "(all but the first 3/10 of the tokens) into the Infinity Cache; the row kernel then reads "
+                       "them again from there. Algorithmic bytes here are the layout's alone (x belongs to the "
+                       "dispatch).",
+    "layout_rank": "Most of these bytes are the fused call's prefetch blocks reading 40 MB of token rows into the "
+                   "Infinity Cache while the rank kernel runs; the row kernel then reads them again from there. "
+                   "Algorithmic bytes here are the ids alone (x belongs to the dispatch).",
+    "layout_index": "Most of these bytes are the fused call's prefetch blocks reading 60 MB of token rows into the "
+                    "Infinity Cache while the index kernel runs; the row kernel then reads them again from there. "
+                    "Algorithmic bytes here are the maps alone (x belongs to the dispatch).",
+}
+
+
 def kernel_bytes(bench):
     """Algorithmic bytes per launch of each library kernel a benchmark line ran."""
     ab = bench["path"]["algorithmic_bytes"]
@@ -544,6 +561,9 @@ def summarize(run_dir, calib_mib):
                       f"{cf:,.1f} KiB and its WRITE_SIZE {cw:,.1f} KiB, so FETCH_SIZE is multiplied by "
                       f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f}. Both count L2 requests to the data "
                       f"fabric: an Infinity Cache hit and an HBM access look the same to them.", ""]
+            fused = isinstance(bench["path"]["calls"], str) and bench["path"]["calls"].startswith("moe_dispatch_fused")
+            if fused and short in PREFETCH_NOTES and a and rec["ratio"] > 2:
+                lines += [PREFETCH_NOTES[short], ""]
             for tag, label, sub in (("counters", "back-to-back steps", "pmc_extra"),
                                     ("counters_cold", "steps after a cache flush", "pmc_extra_cold")):
                 cs = rec.get(tag)

@@ -221,7 +221,10 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t num_tokens, const uin
  * of moe_dispatch over every compute unit.  So a call whose x was evicted
  * from the caches reads most of it from HBM while the layout runs, not behind
  * its own row stores.  Batches beyond the one-launch
- * limits run the layout and dispatch kernels back to back.
+ * limits run the two-launch layout and the row kernel; from 8 tokens per
+ * compute unit on (num_cus = 0, at most 512 experts) prefetch blocks in the
+ * two layout kernels read 100 MB of x (after the first 3/10 of the tokens)
+ * into the Infinity Cache meanwhile.
  */
 moe_status_t moe_dispatch_fused(const moe_config_t *cfg, int32_t num_tokens, const int32_t *topk_idx,
                                 const uint16_t *x, const float *topk_w, const moe_handle_t *handle,
